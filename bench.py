@@ -1,0 +1,280 @@
+"""Benchmark of the Star Attention two-phase hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input, inputs already
+resident in HBM:
+  Phase 1  star_phase1_encode over the whole context (one kernel launch),
+  Phase 2  query encoding: one star_phase2_partial per context shard, one for the query
+           host's own cache, then star_softmax_merge,
+           then decode_steps x star_decode_step (append + split-KV partials + merge).
+
+Prints ONE JSON line.  `value` is context tokens per second of the whole step
+(L / step time).  `roofline` describes the dominant kernel (the Phase-1 MFMA kernel):
+algorithmic flops per launch / its average launch time measured with HIP events on the
+launch stream, against the bf16 dense MFMA peak.  `decode` reports the decode step's
+K/V stream rate (warm: inside the step; cold: after overwriting 1 GiB so the 256 MB
+last-level cache holds no K/V).  `cpu_baseline` times the fp64 oracle on a bounded sample
+of Phase-1 rows on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Phase-1 context tokens/s + MFMA %peak; Phase-2 decode KV GB/s (%HBM), 1 GPU"
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
+PHASE1_KERNEL = "attn_mfma_kernel<0>"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "phase1_8b_32k_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_phase1_amd", "csrc", f)
+                  for f in ("prefill.hip", "common.h", "internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(launch_flops_unit_bytes=None):
+    """HBM bytes per Phase-1 launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    text = open(PROFILE_TRAFFIC).read()
+    m = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="8b_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-reps", type=int, default=8)
+    ap.add_argument("--only", choices=["all", "phase1", "decode"], default="all",
+                    help="restrict the timed step (for profiling runs); the JSON line is always the full step")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the whole path on a single MI355X "
+              "(--gpus %d requested); see the sharding design in DESIGN.md" % args.gpus)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import numpy as np
+    import torch
+
+    import block_sparse_long_phase1_amd as sa
+    from block_sparse_long_phase1_amd import inputs as sin
+    from block_sparse_long_phase1_amd.configs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print("bench: config %s, generating inputs" % cfg.name, file=sys.stderr, flush=True)
+    x = sin.all_inputs(cfg, dev)
+    q, k, v = x["q_ctx"], x["k_ctx"], x["v_ctx"]
+    bounds = cfg.bounds()
+    dt = q.dtype
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.hq, cfg.L), dtype=torch.float32, device=dev)
+    k_tail = torch.zeros((cfg.hkv, cfg.tail_cap, cfg.d), dtype=dt, device=dev)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :cfg.lq] = x["k_qry"]
+    v_tail[:, :cfg.lq] = x["v_qry"]
+    S = len(bounds) - 1
+    P = S + 1
+    pa = torch.empty((P, cfg.hq, cfg.lq, cfg.d), dtype=torch.float32, device=dev)
+    pm = torch.empty((P, cfg.hq, cfg.lq), dtype=torch.float32, device=dev)
+    pl = torch.empty_like(pm)
+    ws_p = max(sa.star_phase2_workspace_bytes(cfg.lq, hi - lo, cfg.hq, cfg.hkv, cfg.d)
+               for lo, hi in zip(bounds[:-1], bounds[1:]))
+    ws_p = max(ws_p, sa.star_phase2_workspace_bytes(cfg.lq, cfg.lq, cfg.hq, cfg.hkv, cfg.d))
+    ws_part = torch.empty(max(ws_p, 16), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(max(16, sa.star_decode_workspace_bytes(cfg.L, cfg.tail_cap, S, cfg.hq, cfg.hkv, cfg.d)),
+                         dtype=torch.uint8, device=dev)
+    oq = torch.empty((cfg.hq, cfg.lq, cfg.d), dtype=dt, device=dev)
+    lq_lse = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device=dev)
+    od = torch.empty((cfg.decode_steps, cfg.hq, cfg.d), dtype=dt, device=dev)
+    ld = torch.empty((cfg.decode_steps, cfg.hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def phase1():
+        sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor, o=o, lse=lse, stream=stream)
+
+    def query_phase():
+        for r, (lo, hi) in enumerate(zip(bounds[:-1], bounds[1:])):
+            sa.star_phase2_partial(x["q_qry"], k[:, lo:], v[:, lo:], cfg.L * cfg.d, hi - lo, -1,
+                                   a_out=pa[r], m_out=pm[r], l_out=pl[r], workspace=ws_part, stream=stream)
+        sa.star_phase2_partial(x["q_qry"], k_tail, v_tail, cfg.tail_cap * cfg.d, cfg.lq, 0,
+                               a_out=pa[S], m_out=pm[S], l_out=pl[S], workspace=ws_part, stream=stream)
+        sa.star_softmax_merge(pa, pm, pl, o=oq, lse=lq_lse, stream=stream)
+
+    def decode(t):
+        sa.star_decode_step(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k, v, bounds, k_tail, v_tail,
+                            cfg.lq + t, o=od[t], lse=ld[t], workspace=ws_dec, stream=stream)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    p1_ms, q_ms, dec_ms = [], [], []
+
+    def step(timed):
+        if args.only in ("all", "phase1"):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            phase1()
+            e1.record(stream)
+        if args.only == "all":
+            e2 = ev()
+            query_phase()
+            e2.record(stream)
+        if args.only in ("all", "decode"):
+            e3 = ev()
+            e3.record(stream)
+            for t in range(cfg.decode_steps):
+                decode(t)
+            e4 = ev()
+            e4.record(stream)
+        if timed:
+            return (e0, e1, e2, e3, e4) if args.only == "all" else None
+        return None
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        evs.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    print("bench: %d timed steps, %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr, flush=True)
+    if args.only != "all":
+        return
+    for e0, e1, e2, e3, e4 in evs:
+        p1_ms.append(e0.elapsed_time(e1))
+        q_ms.append(e1.elapsed_time(e2))
+        dec_ms.append(e3.elapsed_time(e4))
+
+    # ---- cold-cache decode: overwrite 1 GiB before each timed step (untimed)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for r in range(args.cold_reps):
+        flush.fill_(float(r))
+        t = r % cfg.decode_steps
+        a, b = ev(), ev()
+        a.record(stream)
+        decode(t)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append((a.elapsed_time(b), cfg.decode_step_bytes(t)))
+    del flush
+
+    flops = cfg.phase1_flops()
+    p1_avg = float(np.mean(p1_ms))
+    achieved = flops / (p1_avg * 1e-3)
+    dec_bytes = sum(cfg.decode_step_bytes(t) for t in range(cfg.decode_steps))
+    dec_avg = float(np.mean(dec_ms))
+    warm_bw = dec_bytes / (dec_avg * 1e-3)
+    cold_bw = sum(bb for _, bb in cold) / (sum(ms for ms, _ in cold) * 1e-3)
+    traffic = read_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": cfg.L / (ms_per_step * 1e-3),
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) post-rotary Q/K/V, one attention layer)",
+        "config": {"workload": "%s: Hq=%d Hkv=%d d=%d L=%d block=anchor=%d, %d shards, lq=%d, %d decode steps"
+                               % (cfg.name, cfg.hq, cfg.hkv, cfg.d, cfg.L, cfg.block, cfg.shards, cfg.lq,
+                                  cfg.decode_steps),
+                   "L": cfg.L, "block": cfg.block, "anchor": cfg.anchor, "hq": cfg.hq, "hkv": cfg.hkv,
+                   "head_dim": cfg.d, "lq": cfg.lq, "decode_steps": cfg.decode_steps, "shards": cfg.shards},
+        "roofline": {"bound": "mfma", "kernel": PHASE1_KERNEL, "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS,
+                     "traffic": traffic, "flops_per_launch": flops, "launch_ms": p1_avg},
+        "phase1": {"ms": p1_avg, "context_tokens_per_s": cfg.L / (p1_avg * 1e-3),
+                   "tflops": achieved / 1e12, "mfma_frac": achieved / PEAK_BF16_FLOPS},
+        "query_phase": {"ms": float(np.mean(q_ms)), "tflops": cfg.phase2_query_flops() / (np.mean(q_ms) * 1e-3) / 1e12},
+        "decode": {"steps": cfg.decode_steps, "ms_per_token": dec_avg / cfg.decode_steps,
+                   "bytes_per_token": dec_bytes / cfg.decode_steps,
+                   "warm_GBps": warm_bw / 1e9, "warm_hbm_frac": warm_bw / PEAK_HBM_BYTES,
+                   "cold_GBps": cold_bw / 1e9, "cold_hbm_frac": cold_bw / PEAK_HBM_BYTES,
+                   "cold_ms_per_token": float(np.mean([ms for ms, _ in cold]))},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, q, k, v, seconds):
+    """fp64 oracle on the host: Phase-1 rows (all q heads each) for about `seconds` of CPU
+    time, scaled to context tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    kh, vh = k.cpu(), v.cpu()
+    rng = np.random.default_rng(cfg.seed)
+    done, elapsed, batch = 0, 0.0, 32
+    while elapsed < seconds:
+        rows = np.sort(rng.choice(cfg.L, size=batch, replace=False)).astype(np.int64)
+        qs = q[:, torch.from_numpy(rows).to(q.device)].cpu()
+        t0 = time.perf_counter()
+        oracle.phase1(qs, kh, vh, cfg.block, cfg.anchor, rows=rows, q_sampled=True, threads=threads)
+        elapsed += time.perf_counter() - t0
+        done += batch
+        batch = min(batch * 2, 1024)
+    return {"value": done / elapsed, "unit": "context tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d seeded-random Phase-1 context rows x all %d q heads of %s, fp64 C oracle, %.1f s"
+                      % (done, cfg.hq, cfg.name, elapsed)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,106 @@
+// Internal interfaces between the C-ABI layer (star_attn.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace star {
+
+// Arguments of the bf16 MFMA attention kernel (Phase 1 and Phase-2 partials).
+struct AttnMfmaArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t kv_head_stride;   // elements between kv heads
+    int64_t q_rows;           // rows per q head in q (and in the outputs)
+    int hq, hkv, G, rows_per_wg;
+    float scale_log2;         // scale * log2(e)
+    // Phase 1
+    int64_t L, block, anchor;
+    int64_t n_blocks, nt_full, nt_last, nt0, tiles_ge1;
+    uint16_t* o;
+    float* lse;
+    // Phase-2 partial
+    int64_t rows, n_kv, causal_offset, split_len;
+    int64_t n_row_tiles;
+    float* a_out;
+    float* m_out;
+    float* l_out;
+};
+
+bool attn_mfma_supported(int d, int hq, int hkv);
+
+hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint16_t* o, float* lse, int64_t L, int64_t block, int64_t anchor,
+                              int hq, int hkv, float scale, hipStream_t stream);
+
+void partial_mfma_plan(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv,
+                       int* n_row_tiles, int* n_splits, int64_t* split_len);
+
+hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, const uint16_t* k, const uint16_t* v,
+                               int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
+                               int hq, int hkv, float scale, float* a_out, float* m_out, float* l_out,
+                               int n_splits, int64_t split_len, int n_row_tiles, hipStream_t stream);
+
+// Log-space merge of n_parts partials laid out [n_parts][n_rows][d] / [n_parts][n_rows].
+// Writes o ([n_rows][d], fp32 or bf16 per out_bf16), and optionally lse, or (m, l).
+hipError_t launch_merge(const float* a, const float* m, const float* l, int n_parts, int64_t n_rows,
+                        int d, void* o, bool out_bf16, float* lse_out, float* m_out, float* l_out,
+                        hipStream_t stream);
+
+// Split-KV decode (bf16, d = 128): chunk partials for every kv head, plus the append of
+// the new token into the query host's cache.
+struct DecodeChunkPlan {
+    int n_shards;
+    int64_t chunk;                 // keys per chunk
+    int64_t shard_lo[65];          // shard token bounds
+    int32_t chunk_prefix[66];      // first chunk index of each shard; [n_shards] = first tail chunk
+    int32_t n_chunks;              // total chunks including the tail ones
+};
+
+bool decode_bf16_supported(int d, int hq, int hkv);
+int64_t decode_chunk_len(int64_t L, int64_t tail_cap, int32_t hkv);
+hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
+                              const uint16_t* k_ctx, const uint16_t* v_ctx, int64_t L,
+                              uint16_t* k_tail, uint16_t* v_tail, int64_t tail_len, int64_t tail_cap,
+                              int hq, int hkv, float scale, const DecodeChunkPlan& plan,
+                              float* part_a, float* part_m, float* part_l, hipStream_t stream);
+
+// Plain vector path (fp32 or bf16 inputs, any d <= 256 with d % 4 == 0): one wave per row.
+struct RowKeySeg {
+    const void* k;       // base of token 0 of this segment for kv head 0
+    const void* v;
+    int64_t head_stride; // elements between kv heads
+    int64_t n;           // tokens in the segment
+    int64_t causal_lim;  // < 0: all visible; else token t visible to row i iff t <= causal_lim + i
+};
+struct RowAttnArgs {
+    const void* q;
+    int64_t q_rows;      // rows per head in q
+    int hq, hkv, d;
+    int is_bf16;
+    float scale;
+    int mode;            // 0: phase 1 (segments derived per row); 1: explicit segments
+    // mode 0
+    const void* k;
+    const void* v;
+    int64_t L, block, anchor;
+    // mode 1
+    RowKeySeg seg[3];
+    int n_seg;
+    // outputs: o (dtype) + lse, or (a, m, l) fp32
+    void* o;
+    float* lse;
+    float* a_out;
+    float* m_out;
+    float* l_out;
+    int64_t row_offset;  // mode 1: row i uses causal row index i + row_offset
+};
+hipError_t launch_row_attn(const RowAttnArgs& a, int64_t rows, hipStream_t stream);
+
+// Copy n_bytes of k_new / v_new rows into the tail at `tail_len` (vector path append).
+hipError_t launch_tail_append(const void* k_new, const void* v_new, void* k_tail, void* v_tail,
+                              int64_t tail_len, int64_t tail_cap, int hkv, int d, int elem_bytes,
+                              hipStream_t stream);
+
+}  // namespace star

@@ -1,0 +1,299 @@
+// C ABI of libstarattn.so: argument checking, work planning and dispatch to
+// the gfx950 kernels.  Every entry point validates on the host before it
+// enqueues anything, never allocates device memory and never synchronises.
+#include "star_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+star_status_t fail(star_status_t s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+star_status_t ok() {
+    g_last_error.clear();
+    return STAR_OK;
+}
+
+star_status_t hip_fail(hipError_t e, const char* where) {
+    return fail(STAR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(star_dtype_t dt) { return dt == STAR_BF16 ? 2 : 4; }
+
+star_status_t check_heads(int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt) {
+    if (hq < 1 || hkv < 1) return fail(STAR_ERR_INVALID_ARG, "hq (%d) and hkv (%d) must be >= 1", hq, hkv);
+    if (hq % hkv) return fail(STAR_ERR_INVALID_ARG, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
+    if (d < 1) return fail(STAR_ERR_INVALID_ARG, "d (%d) must be >= 1", d);
+    if (dt != STAR_F32 && dt != STAR_BF16) return fail(STAR_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+    if (d > 256 || d % 4)
+        return fail(STAR_ERR_UNSUPPORTED, "head dim %d not supported (need d %% 4 == 0 and d <= 256)", d);
+    return STAR_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout of split partials: A [n][rows][d] fp32, then m [n][rows], then l [n][rows].
+size_t partials_bytes(int64_t n_parts, int64_t n_rows, int32_t d) {
+    return round_up((size_t)n_parts * n_rows * d * 4) + 2 * round_up((size_t)n_parts * n_rows * 4);
+}
+void partials_ptrs(void* ws, int64_t n_parts, int64_t n_rows, int32_t d, float** a, float** m, float** l) {
+    char* base = static_cast<char*>(ws);
+    *a = reinterpret_cast<float*>(base);
+    *m = reinterpret_cast<float*>(base + round_up((size_t)n_parts * n_rows * d * 4));
+    *l = reinterpret_cast<float*>(base + round_up((size_t)n_parts * n_rows * d * 4) +
+                                  round_up((size_t)n_parts * n_rows * 4));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* star_status_str(star_status_t status) {
+    switch (status) {
+        case STAR_OK: return "STAR_OK";
+        case STAR_ERR_INVALID_ARG: return "STAR_ERR_INVALID_ARG";
+        case STAR_ERR_UNSUPPORTED: return "STAR_ERR_UNSUPPORTED";
+        case STAR_ERR_HIP: return "STAR_ERR_HIP";
+        case STAR_ERR_WORKSPACE: return "STAR_ERR_WORKSPACE";
+    }
+    return "STAR_ERR_UNKNOWN";
+}
+
+const char* star_last_error(void) { return g_last_error.c_str(); }
+
+const char* star_version(void) { return "0.1.0"; }
+
+// ------------------------------------------------------------------------ Phase 1
+star_status_t star_phase1_encode(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t L, int64_t block, int64_t anchor, int32_t hq, int32_t hkv,
+                                 int32_t d, star_dtype_t dt, float scale, hipStream_t stream) {
+    try {
+        if (!q || !k || !v || !o) return fail(STAR_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+        if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L (%lld) must be >= 1", (long long)L);
+        if (block < 1) return fail(STAR_ERR_INVALID_ARG, "block (%lld) must be >= 1", (long long)block);
+        if (anchor < 0 || anchor > block)
+            return fail(STAR_ERR_INVALID_ARG, "anchor (%lld) must satisfy 0 <= anchor <= block (%lld)",
+                        (long long)anchor, (long long)block);
+        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        star_status_t s = check_heads(hq, hkv, d, dt);
+        if (s != STAR_OK) return s;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+            (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+            return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+        hipError_t e;
+        if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
+            e = star::launch_phase1_mfma(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                                         L, block, anchor, hq, hkv, scale, stream);
+        } else {
+            star::RowAttnArgs a = {};
+            a.q = q; a.q_rows = L; a.hq = hq; a.hkv = hkv; a.d = d;
+            a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 0;
+            a.k = k; a.v = v; a.L = L; a.block = block; a.anchor = anchor;
+            a.o = o; a.lse = lse;
+            e = star::launch_row_attn(a, L, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "star_phase1_encode launch");
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_phase1_encode: internal error");
+    }
+}
+
+// ------------------------------------------------------------------------ Phase 2 partial
+size_t star_phase2_workspace_bytes(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv, int32_t d) {
+    if (rows < 1 || n_kv < 0 || hq < 1 || hkv < 1 || hq % hkv || d < 1) return 0;
+    if (!star::attn_mfma_supported(d, hq, hkv)) return 0;
+    int nrt, ns;
+    int64_t split_len;
+    star::partial_mfma_plan(rows, n_kv, hq, hkv, &nrt, &ns, &split_len);
+    return ns > 1 ? partials_bytes(ns, (int64_t)hq * rows, d) : 0;
+}
+
+star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, const void* v,
+                                  int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
+                                  int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt, float scale,
+                                  float* a_out, float* m_out, float* l_out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    try {
+        if (!q || !a_out || !m_out || !l_out) return fail(STAR_ERR_INVALID_ARG, "q, a_out, m_out, l_out must be non-null");
+        if (n_kv > 0 && (!k || !v)) return fail(STAR_ERR_INVALID_ARG, "k and v must be non-null when n_kv > 0");
+        if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
+        if (n_kv < 0) return fail(STAR_ERR_INVALID_ARG, "n_kv must be >= 0");
+        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        star_status_t s = check_heads(hq, hkv, d, dt);
+        if (s != STAR_OK) return s;
+        if (hkv > 1 && kv_head_stride < n_kv * d)
+            return fail(STAR_ERR_INVALID_ARG, "kv_head_stride (%lld) smaller than n_kv * d", (long long)kv_head_stride);
+        if (kv_head_stride < 0) return fail(STAR_ERR_INVALID_ARG, "kv_head_stride must be >= 0");
+        if (!aligned16(q) || (k && !aligned16(k)) || (v && !aligned16(v)) || !aligned16(a_out) ||
+            (reinterpret_cast<uintptr_t>(m_out) & 3u) || (reinterpret_cast<uintptr_t>(l_out) & 3u) ||
+            ((kv_head_stride * elem_bytes(dt)) % 16))
+            return fail(STAR_ERR_INVALID_ARG, "pointers and the kv head stride must be 16-byte aligned");
+        hipError_t e;
+        if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
+            int nrt, ns;
+            int64_t split_len;
+            star::partial_mfma_plan(rows, n_kv, hq, hkv, &nrt, &ns, &split_len);
+            if (ns == 1) {
+                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, static_cast<const uint16_t*>(k),
+                                              static_cast<const uint16_t*>(v), kv_head_stride, n_kv, causal_offset,
+                                              hq, hkv, scale, a_out, m_out, l_out, 1, split_len, nrt, stream);
+                if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
+            } else {
+                size_t need = partials_bytes(ns, (int64_t)hq * rows, d);
+                if (!workspace || workspace_bytes < need || !aligned16(workspace))
+                    return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
+                                need, workspace ? workspace_bytes : (size_t)0);
+                float *wa, *wm, *wl;
+                partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
+                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, static_cast<const uint16_t*>(k),
+                                              static_cast<const uint16_t*>(v), kv_head_stride, n_kv, causal_offset,
+                                              hq, hkv, scale, wa, wm, wl, ns, split_len, nrt, stream);
+                if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
+                e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, a_out, false, nullptr, m_out, l_out, stream);
+                if (e != hipSuccess) return hip_fail(e, "star_phase2_partial merge launch");
+            }
+        } else {
+            star::RowAttnArgs a = {};
+            a.q = q; a.q_rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
+            a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 1;
+            a.n_seg = n_kv > 0 ? 1 : 0;
+            a.seg[0].k = k; a.seg[0].v = v; a.seg[0].head_stride = kv_head_stride;
+            a.seg[0].n = n_kv; a.seg[0].causal_lim = causal_offset;
+            a.a_out = a_out; a.m_out = m_out; a.l_out = l_out;
+            e = star::launch_row_attn(a, rows, stream);
+            if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
+        }
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_phase2_partial: internal error");
+    }
+}
+
+// ------------------------------------------------------------------------ merge
+star_status_t star_softmax_merge(const float* a, const float* m, const float* l, int32_t n_parts,
+                                 int32_t hq, int32_t rows, int32_t d, void* o, star_dtype_t out_dt,
+                                 float* lse_out, hipStream_t stream) {
+    try {
+        if (!a || !m || !l || !o) return fail(STAR_ERR_INVALID_ARG, "a, m, l and o must be non-null");
+        if (n_parts < 1) return fail(STAR_ERR_INVALID_ARG, "n_parts must be >= 1");
+        if (hq < 1 || rows < 1) return fail(STAR_ERR_INVALID_ARG, "hq and rows must be >= 1");
+        if (out_dt != STAR_F32 && out_dt != STAR_BF16) return fail(STAR_ERR_INVALID_ARG, "unknown dtype");
+        if (d < 4 || d % 4 || d > 1024) return fail(STAR_ERR_UNSUPPORTED, "merge needs d %% 4 == 0 and 4 <= d <= 1024");
+        if (!aligned16(a) || !aligned16(o) || (reinterpret_cast<uintptr_t>(m) & 3u) ||
+            (reinterpret_cast<uintptr_t>(l) & 3u) || (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)))
+            return fail(STAR_ERR_INVALID_ARG, "a and o must be 16-byte aligned");
+        hipError_t e = star::launch_merge(a, m, l, n_parts, (int64_t)hq * rows, d, o, out_dt == STAR_BF16,
+                                          lse_out, nullptr, nullptr, stream);
+        if (e != hipSuccess) return hip_fail(e, "star_softmax_merge launch");
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_softmax_merge: internal error");
+    }
+}
+
+// ------------------------------------------------------------------------ decode
+size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards, int32_t hq,
+                                   int32_t hkv, int32_t d) {
+    if (L < 1 || tail_cap < 1 || n_shards < 1 || hq < 1 || hkv < 1 || hq % hkv || d < 1) return 0;
+    const int64_t ch = star::decode_chunk_len(L, tail_cap, hkv);
+    const int64_t n_max = (L + ch - 1) / ch + n_shards + (tail_cap + ch - 1) / ch + 1;
+    return partials_bytes(n_max, hq, d);
+}
+
+star_status_t star_decode_step(const void* q_new, const void* k_new, const void* v_new,
+                               const void* k_ctx, const void* v_ctx, int64_t L,
+                               const int64_t* shard_bounds, int32_t n_shards,
+                               void* k_tail, void* v_tail, int64_t tail_len, int64_t tail_cap,
+                               int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt, float scale,
+                               void* o, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    try {
+        if (!q_new || !k_new || !v_new || !k_ctx || !v_ctx || !k_tail || !v_tail || !o || !shard_bounds)
+            return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+        if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
+        if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
+        if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
+            return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
+        for (int r = 0; r < n_shards; ++r)
+            if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
+        if (tail_len < 0 || tail_cap < 1 || tail_len + 1 > tail_cap)
+            return fail(STAR_ERR_INVALID_ARG, "need 0 <= tail_len < tail_cap (tail_len %lld, tail_cap %lld)",
+                        (long long)tail_len, (long long)tail_cap);
+        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        star_status_t s = check_heads(hq, hkv, d, dt);
+        if (s != STAR_OK) return s;
+        if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_ctx) || !aligned16(v_ctx) ||
+            !aligned16(k_tail) || !aligned16(v_tail) || !aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+            return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+        hipError_t e;
+        if (dt == STAR_BF16 && star::decode_bf16_supported(d, hq, hkv)) {
+            star::DecodeChunkPlan plan = {};
+            plan.n_shards = n_shards;
+            plan.chunk = star::decode_chunk_len(L, tail_cap, hkv);
+            int64_t nc = 0;
+            for (int r = 0; r < n_shards; ++r) {
+                plan.shard_lo[r] = shard_bounds[r];
+                plan.chunk_prefix[r] = (int32_t)nc;
+                nc += (shard_bounds[r + 1] - shard_bounds[r] + plan.chunk - 1) / plan.chunk;
+            }
+            plan.shard_lo[n_shards] = shard_bounds[n_shards];
+            plan.chunk_prefix[n_shards] = (int32_t)nc;
+            nc += (tail_len + 1 + plan.chunk - 1) / plan.chunk;
+            plan.chunk_prefix[n_shards + 1] = (int32_t)nc;
+            plan.n_chunks = (int32_t)nc;
+            const size_t need = partials_bytes(nc, hq, d);
+            if (!workspace || workspace_bytes < need || !aligned16(workspace))
+                return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                            workspace ? workspace_bytes : (size_t)0);
+            float *wa, *wm, *wl;
+            partials_ptrs(workspace, nc, hq, d, &wa, &wm, &wl);
+            e = star::launch_decode_bf16(static_cast<const uint16_t*>(q_new), static_cast<const uint16_t*>(k_new),
+                                         static_cast<const uint16_t*>(v_new), static_cast<const uint16_t*>(k_ctx),
+                                         static_cast<const uint16_t*>(v_ctx), L, static_cast<uint16_t*>(k_tail),
+                                         static_cast<uint16_t*>(v_tail), tail_len, tail_cap, hq, hkv, scale, plan,
+                                         wa, wm, wl, stream);
+            if (e != hipSuccess) return hip_fail(e, "star_decode_step launch");
+            e = star::launch_merge(wa, wm, wl, (int)nc, hq, d, o, true, lse, nullptr, nullptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "star_decode_step merge launch");
+        } else {
+            e = star::launch_tail_append(k_new, v_new, k_tail, v_tail, tail_len, tail_cap, hkv, d, elem_bytes(dt), stream);
+            if (e != hipSuccess) return hip_fail(e, "star_decode_step append launch");
+            star::RowAttnArgs a = {};
+            a.q = q_new; a.q_rows = 1; a.hq = hq; a.hkv = hkv; a.d = d;
+            a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 1;
+            a.n_seg = 2;
+            a.seg[0].k = k_ctx; a.seg[0].v = v_ctx; a.seg[0].head_stride = L * d;
+            a.seg[0].n = L; a.seg[0].causal_lim = -1;
+            a.seg[1].k = k_tail; a.seg[1].v = v_tail; a.seg[1].head_stride = tail_cap * d;
+            a.seg[1].n = tail_len + 1; a.seg[1].causal_lim = -1;
+            a.o = o; a.lse = lse;
+            e = star::launch_row_attn(a, 1, stream);
+            if (e != hipSuccess) return hip_fail(e, "star_decode_step launch");
+        }
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_decode_step: internal error");
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+/*
+ * star_attn.h -- C ABI of libstarattn.so: the Star Attention two-phase
+ * attention hot path on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (pages, cited by title and section):
+ *   [SUM]    "Star Attention: Efficient LLM Inference over Long Sequences",
+ *            paper-graph-ui long-form summary of arXiv 2411.17116, section 3.4
+ *            "Detailed, Sentence-Based Technical Breakdown".
+ *   [README] "NVIDIA/Star-Attention" (shadowgraph.io mirror of the project
+ *            README), section "Two Phases of Star Attention".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Batch 1, head-major, contiguous: queries [Hq, rows, d], keys and
+ *   values [Hkv, tokens, d].  Grouped-query attention maps q head h to kv
+ *   head h / (Hq / Hkv) (contiguous groups).  Hq must be a multiple of Hkv.
+ * Scale.  Scores are scale * <q, k>; pass scale = 1/sqrt(d) for the pages'
+ *   attention ([SUM] 3.4 "The Attention Decomposition").  All logs and
+ *   log-sum-exps are natural logs of the scaled scores.
+ * Softmax statistics.  A partial result over a key partition is (A, m, l):
+ *   A is normalised over that partition alone, m is the largest scaled score
+ *   and l = sum exp(score - m), so the pages' s_h equals e^m * l.  An empty
+ *   partition is A = 0, m = -inf, l = 0 and weighs nothing in a merge.
+ * Types.  STAR_BF16 inputs are accumulated in fp32 (the fast MFMA kernels
+ *   need d = 128); STAR_F32 inputs take a plain vector path (d <= 256, any
+ *   multiple of 4).  Partials and LSEs are always fp32.
+ * Memory and ownership.  Every pointer not marked "host" is device memory
+ *   owned by the caller, 16-byte aligned.  The library never allocates or
+ *   frees device memory and keeps no state between calls; entry points that
+ *   need scratch take a caller-provided workspace whose size the matching
+ *   *_workspace_bytes() call returns.
+ * Streams and errors.  Every call only enqueues work on `stream` and returns
+ *   without synchronising.  Arguments are checked on the host before anything
+ *   is enqueued: a bad argument returns STAR_ERR_INVALID_ARG, a shape the
+ *   kernels do not cover returns STAR_ERR_UNSUPPORTED, a short workspace
+ *   STAR_ERR_WORKSPACE, and a failed launch STAR_ERR_HIP.  On any error
+ *   nothing has been enqueued except, for STAR_ERR_HIP, work launched before
+ *   the failing launch.  star_last_error() describes the last failure on the
+ *   calling thread.  No C++ exception crosses this interface.  Calls are
+ *   thread-safe; calls that write the same buffers must be ordered by the
+ *   caller's streams.
+ */
+#ifndef STAR_ATTN_H
+#define STAR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STAR_OK = 0,
+    STAR_ERR_INVALID_ARG = 1,
+    STAR_ERR_UNSUPPORTED = 2,
+    STAR_ERR_HIP = 3,
+    STAR_ERR_WORKSPACE = 4
+} star_status_t;
+
+typedef enum { STAR_F32 = 0, STAR_BF16 = 1 } star_dtype_t;
+
+/* Static name of a status code. */
+const char *star_status_str(star_status_t status);
+
+/* Human-readable description of the last failure on the calling thread
+ * ("" if none).  The string stays valid until the thread's next call. */
+const char *star_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *star_version(void);
+
+/*
+ * Phase 1: anchored blockwise-local context encoding.
+ * [SUM] 3.4 Phase 1 Steps 1-5; [README] "Phase 1 - Context Encoding".
+ *
+ * The context of L tokens is cut into n = ceil(L / block) contiguous blocks
+ * (the last may be shorter).  Block 0 is attended causally on its own; every
+ * later block i is attended causally after the anchor, i.e. the row of
+ * context position p in block i >= 1 sees the anchor tokens [0, anchor) and
+ * its own block's tokens [i*block, p].  The anchor keeps its original
+ * positions, so with post-rotary inputs its keys are the block-0 keys and are
+ * read in place; anchor rows of later blocks are not produced and anchor
+ * keys/values are never copied, so k and v, unchanged, are the Phase-2
+ * context cache (each token once).
+ *
+ *   q    [hq, L, d]    queries of the context tokens (dt)
+ *   k, v [hkv, L, d]   keys / values of the context tokens (dt)
+ *   o    [hq, L, d]    output (dt, round-to-nearest-even)
+ *   lse  [hq, L]       fp32 log-sum-exp of each row's scores, or NULL
+ *   L >= 1, block >= 1, 0 <= anchor <= block.
+ * One kernel launch.
+ */
+star_status_t star_phase1_encode(const void *q, const void *k, const void *v,
+                                 void *o, float *lse,
+                                 int64_t L, int64_t block, int64_t anchor,
+                                 int32_t hq, int32_t hkv, int32_t d,
+                                 star_dtype_t dt, float scale, hipStream_t stream);
+
+/*
+ * Phase 2, one partition ("host"): local attention of the query rows over
+ * one KV partition and its softmax statistics.
+ * [SUM] 3.4 Phase 2 Step 3 (the A_h and s_h equations); [README] "Phase 2".
+ *
+ *   q [hq, rows, d] (dt); rows >= 1
+ *   k, v: partition token t of kv head g is at element offset
+ *         g * kv_head_stride + t * d, for 0 <= t < n_kv (n_kv >= 0).  A
+ *         context shard [lo, hi) of a [hkv, L, d] cache is k + lo*d with
+ *         kv_head_stride = L*d and n_kv = hi - lo.
+ *   causal_offset < 0: every row sees every partition token; otherwise row i
+ *         sees token t only if t <= causal_offset + i (the query host's own
+ *         cache, where query tokens are causal among themselves).
+ *   a_out [hq, rows, d], m_out [hq, rows], l_out [hq, rows]: fp32 (A, m, l).
+ *   workspace: star_phase2_workspace_bytes(rows, n_kv, hq, hkv, d) bytes
+ *         (may be 0, then workspace may be NULL).
+ * One or two kernel launches (a key-split pass and its merge).
+ */
+size_t star_phase2_workspace_bytes(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv, int32_t d);
+
+star_status_t star_phase2_partial(const void *q, int32_t rows,
+                                  const void *k, const void *v,
+                                  int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
+                                  int32_t hq, int32_t hkv, int32_t d,
+                                  star_dtype_t dt, float scale,
+                                  float *a_out, float *m_out, float *l_out,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Global aggregation of partitions in log space.
+ * [README] "Phase 2" (s_global = sum s_h, A_global = sum (s_h/s_global) A_h);
+ * [SUM] 3.4 Phase 2 Step 5 (the same sum kept in log space).
+ *
+ *   a [n_parts, hq, rows, d], m and l [n_parts, hq, rows]: fp32 partials.
+ *   o [hq, rows, d] (out_dt), lse_out [hq, rows] fp32 or NULL.
+ *   With M = max_p m_p and w_p = l_p e^{m_p - M}:
+ *   o = sum w_p A_p / sum w_p and lse = M + log sum w_p.  Rows whose
+ *   partitions are all empty get o = 0 and lse = -inf.
+ * One kernel launch.
+ */
+star_status_t star_softmax_merge(const float *a, const float *m, const float *l, int32_t n_parts,
+                                 int32_t hq, int32_t rows, int32_t d,
+                                 void *o, star_dtype_t out_dt, float *lse_out, hipStream_t stream);
+
+/*
+ * Phase 2, one generated token on the query host.
+ * [SUM] 3.4 Phase 2 Steps 3-5 and 7; [README] "Phase 2".
+ *
+ * Appends the new token's k/v to the query host's cache (the only cache that
+ * grows) and computes its attention over every context token plus the query
+ * host's cache including itself, as per-partition partials merged in log
+ * space.  The context cache is split into the n_shards host partitions
+ * given by shard_bounds; each is further split into key chunks internally.
+ *
+ *   q_new [hq, d], k_new / v_new [hkv, d]   the new token (dt)
+ *   k_ctx, v_ctx [hkv, L, d]                context cache (dt), L >= 1
+ *   shard_bounds (host) int64[n_shards + 1]: 0 = b_0 <= b_1 <= ... <= b_S = L;
+ *                                            1 <= n_shards <= 64
+ *   k_tail, v_tail [hkv, tail_cap, d]       query-host cache (dt); entries
+ *                                           [0, tail_len) are valid on entry,
+ *                                           entry tail_len is written
+ *   o [hq, d] (dt), lse [hq] fp32 or NULL
+ *   workspace: star_decode_workspace_bytes(L, tail_cap, n_shards, hq, hkv, d)
+ *   0 <= tail_len < tail_cap.
+ * Two kernel launches (chunk partials with the append, then the merge).
+ */
+size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards,
+                                   int32_t hq, int32_t hkv, int32_t d);
+
+star_status_t star_decode_step(const void *q_new, const void *k_new, const void *v_new,
+                               const void *k_ctx, const void *v_ctx, int64_t L,
+                               const int64_t *shard_bounds, int32_t n_shards,
+                               void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
+                               int32_t hq, int32_t hkv, int32_t d,
+                               star_dtype_t dt, float scale,
+                               void *o, float *lse,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STAR_ATTN_H */

@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports every declared entry point and rejects bad arguments
+on the host (no GPU needed: every call here fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_phase1_amd as sa
+from block_sparse_long_phase1_amd import build as sa_build
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "star_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sa.LIB_PATH):
+        sa_build.build()
+    return sa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(star_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.star_status_str(0) == b"STAR_OK"
+    assert lib.star_status_str(1) == b"STAR_ERR_INVALID_ARG"
+    assert lib.star_status_str(4) == b"STAR_ERR_WORKSPACE"
+    assert lib.star_version().count(b".") == 2
+
+
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: validation fails first
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 1, 0.1), 1),          # null q
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 0, 32, 32, 4, 2, 128, 1, 0.1), 1),           # L < 1
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 33, 4, 2, 128, 1, 0.1), 1),          # anchor > block
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, -1, 4, 2, 128, 1, 0.1), 1),          # anchor < 0
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 0, 0, 4, 2, 128, 1, 0.1), 1),            # block < 1
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 5, 2, 128, 1, 0.1), 1),          # hq % hkv
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 130, 1, 0.1), 2),          # d unsupported
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 7, 0.1), 1),          # bad dtype
+    ((ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 1, 0.1), 1),  # misaligned
+    ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 1, float("inf")), 1),  # bad scale
+])
+def test_phase1_validation(lib, args, expect):
+    st = lib.star_phase1_encode(*args, NULL)
+    assert st == expect
+    assert lib.star_last_error() != b""
+
+
+def test_partial_and_merge_validation(lib):
+    p = lib.star_phase2_partial
+    assert p(NULL, 4, FAKE, FAKE, 1024, 8, -1, 4, 2, 128, 1, 0.1, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1
+    assert p(FAKE, 0, FAKE, FAKE, 1024, 8, -1, 4, 2, 128, 1, 0.1, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1
+    assert p(FAKE, 4, FAKE, FAKE, 100, 8, -1, 4, 2, 128, 1, 0.1, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1  # stride < n_kv*d
+    assert p(FAKE, 4, FAKE, FAKE, 1028, 8, -1, 4, 2, 128, 1, 0.1, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1  # stride*2 % 16
+    big = 1 << 20
+    need = lib.star_phase2_workspace_bytes(128, big, 32, 8, 128)
+    assert need > 0
+    assert p(FAKE, 128, FAKE, FAKE, big * 128, big, -1, 32, 8, 128, 1, 0.1, FAKE, FAKE, FAKE,
+             FAKE, need - 1, NULL) == 4
+    m = lib.star_softmax_merge
+    assert m(FAKE, FAKE, FAKE, 0, 4, 1, 128, FAKE, 1, NULL, NULL) == 1
+    assert m(FAKE, FAKE, FAKE, 2, 4, 1, 6, FAKE, 1, NULL, NULL) == 2
+    assert m(NULL, FAKE, FAKE, 2, 4, 1, 128, FAKE, 1, NULL, NULL) == 1
+
+
+def test_decode_validation(lib):
+    d = lib.star_decode_step
+    B = ctypes.c_int64 * 3
+    good = B(0, 50, 100)
+    args = lambda bounds, n_sh, tl, tc, ws: (FAKE, FAKE, FAKE, FAKE, FAKE, 100, bounds, n_sh, FAKE, FAKE,
+                                            tl, tc, 4, 2, 128, 1, 0.1, FAKE, NULL, FAKE, ws, NULL)
+    assert d(*args(B(0, 60, 50), 2, 0, 8, 1 << 30)) == 1          # not monotone
+    assert d(*args(B(0, 50, 99), 2, 0, 8, 1 << 30)) == 1          # does not end at L
+    assert d(*args(B(1, 50, 100), 2, 0, 8, 1 << 30)) == 1         # does not start at 0
+    assert d(*args(good, 2, 8, 8, 1 << 30)) == 1                   # tail full
+    assert d(*args(good, 2, -1, 8, 1 << 30)) == 1                  # negative tail
+    assert d(*args(good, 0, 0, 8, 1 << 30)) == 1                   # no shards
+    assert d(*args(good, 65, 0, 8, 1 << 30)) == 1                  # too many shards
+    assert d(*args(good, 2, 0, 8, 16)) == 4                        # workspace too small
+
+
+def test_workspace_queries(lib):
+    assert lib.star_decode_workspace_bytes(32768, 160, 4, 32, 8, 128) > 0
+    assert lib.star_decode_workspace_bytes(0, 160, 4, 32, 8, 128) == 0
+    assert lib.star_phase2_workspace_bytes(128, 0, 32, 8, 128) == 0
+    assert lib.star_phase2_workspace_bytes(16, 2048, 1, 1, 64) == 0  # vector path needs none
+
+
+def test_binding_names_match_abi():
+    for n in declared_functions():
+        if n in ("star_status_str", "star_last_error", "star_version"):
+            continue
+        assert hasattr(sa, n), n

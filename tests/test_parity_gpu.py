@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle on the same
+seeded inputs.  Sizes span several tiles and ragged tails so the oracle finishes in seconds.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_phase1_amd as sa
+import oracle
+from block_sparse_long_phase1_amd.configs import CONFIGS, StarConfig, shard_bounds
+from block_sparse_long_phase1_amd import inputs as sin
+from tests._parity import assert_lse, assert_out, flush_print, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _cfg(hq, hkv, L, b, a, d=128, dtype="bf16", lq=16, T=3, S=2, seed=7, needle=False):
+    return StarConfig("test", hq=hq, hkv=hkv, d=d, L=L, block=b, anchor=a, lq=lq, decode_steps=T,
+                      shards=S, dtype=dtype, needle=needle, seed=seed)
+
+
+def test_native_library_is_the_in_tree_build():
+    lib = sa.load_library()
+    assert lib._name == sa.LIB_PATH
+    assert torch.cuda.is_available()
+
+
+# ----------------------------------------------------------------------------- Phase 1
+PHASE1_CASES = [
+    # hq, hkv, L, block, anchor
+    (8, 2, 1000, 320, 320),    # G=4, ragged last block (40 rows), anchor = block
+    (8, 2, 1000, 320, 200),    # anchor < block, not a multiple of the key tile
+    (8, 2, 1000, 320, 0),      # no anchor: block-diagonal causal
+    (8, 2, 700, 1024, 1024),   # one block covers the context: global causal
+    (16, 2, 600, 256, 256),    # G=8
+    (2, 2, 500, 200, 200),     # G=1
+    (4, 2, 513, 128, 77),      # G=2, ragged everything
+    (4, 1, 1, 1, 1),           # a single token
+    (4, 2, 97, 1, 1),          # every token its own block
+]
+
+
+@pytest.mark.parametrize("hq,hkv,L,b,a", PHASE1_CASES)
+def test_phase1_bf16(hq, hkv, L, b, a):
+    flush_print("phase1 bf16", hq, hkv, L, b, a)
+    cfg = _cfg(hq, hkv, L, b, a)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    o, lse = sa.star_phase1_encode(q, k, v, b, a)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase1(q.cpu(), k.cpu(), v.cpu(), b, a)
+    assert_out(o, ro, "O")
+    assert_lse(lse, rl, "LSE")
+
+
+@pytest.mark.parametrize("b", [512, 2048])
+def test_phase1_f32_tiny(b):
+    cfg = CONFIGS["tiny_f32"]
+    flush_print("phase1 f32", cfg.name, b)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    o, lse = sa.star_phase1_encode(q, k, v, b, min(b, cfg.anchor))
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase1(q.cpu(), k.cpu(), v.cpu(), b, min(b, cfg.anchor))
+    assert_out(o, ro, "O", max_abs=1e-5, mean_abs=1e-6)
+    assert_lse(lse, rl, "LSE", rel=1e-6)
+
+
+def test_phase1_bf16_vector_path_d64():
+    """bf16 with d=64 takes the vector path; same reading, same bar."""
+    cfg = _cfg(4, 2, 300, 128, 128, d=64)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    o, lse = sa.star_phase1_encode(q, k, v, 128, 128)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase1(q.cpu(), k.cpu(), v.cpu(), 128, 128)
+    assert_out(o, ro, "O")
+    assert_lse(lse, rl, "LSE")
+
+
+def test_phase1_locality_bitwise():
+    """Keys outside a row's visible set cannot change its output, bit for bit."""
+    cfg = _cfg(8, 2, 768, 256, 256)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    o1, l1 = sa.star_phase1_encode(q, k, v, 256, 256)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 256:512] = -k2[:, 256:512]          # block 1 is invisible to block 2
+    v2[:, 256:512] = 3.0
+    o2, l2 = sa.star_phase1_encode(q, k2, v2, 256, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, 512:], o2[:, 512:]) and torch.equal(l1[:, 512:], l2[:, 512:])
+    assert torch.equal(o1[:, :256], o2[:, :256])
+    assert not torch.equal(l1[:, 256:512], l2[:, 256:512])
+
+
+# ----------------------------------------------------------------------------- Phase 2 partial
+PARTIAL_CASES = [
+    # hq, hkv, rows, T_total, lo, hi, causal_offset
+    (8, 2, 128, 1200, 100, 1100, -1),   # shard view inside a longer cache, several splits
+    (8, 2, 100, 3000, 0, 3000, -1),     # ragged rows, many splits
+    (8, 2, 70, 80, 0, 70, 0),           # query host's own cache: causal among the rows
+    (8, 2, 40, 200, 0, 120, 5),         # causal with an offset
+    (16, 2, 33, 500, 17, 417, -1),      # G=8
+    (8, 2, 16, 64, 10, 10, -1),         # empty partition
+]
+
+
+@pytest.mark.parametrize("hq,hkv,rows,T,lo,hi,off", PARTIAL_CASES)
+def test_phase2_partial_bf16(hq, hkv, rows, T, lo, hi, off):
+    flush_print("partial", hq, hkv, rows, T, lo, hi, off)
+    cfg = _cfg(hq, hkv, T, T, T, seed=11)
+    q = sin.randn(cfg, "q_qry", (hq, rows, 128), DEV)
+    k = sin.randn(cfg, "k_ctx", (hkv, T, 128), DEV)
+    v = sin.randn(cfg, "v_ctx", (hkv, T, 128), DEV)
+    a, m, l = sa.star_phase2_partial(q, k[:, lo:], v[:, lo:], T * 128, hi - lo, off)
+    torch.cuda.synchronize()
+    ra, rm, rl = oracle.partial(q.cpu(), k.cpu(), v.cpu(), lo, hi, off)
+    if hi == lo:
+        assert torch.all(a == 0) and torch.all(torch.isneginf(m)) and torch.all(l == 0)
+        return
+    assert_out(a, ra, "A")
+    assert_lse(m + torch.log(l), rm + np.log(rl), "partial LSE")
+    assert_lse(m, rm, "m (largest scaled score)")
+
+
+def test_phase2_partial_f32():
+    cfg = CONFIGS["tiny_f32"]
+    q = sin.randn(cfg, "q_qry", (1, 16, 64), DEV)
+    k = sin.randn(cfg, "k_ctx", (1, 2048, 64), DEV)
+    v = sin.randn(cfg, "v_ctx", (1, 2048, 64), DEV)
+    for lo, hi, off in [(0, 1024, -1), (1024, 2048, -1), (0, 16, 0)]:
+        a, m, l = sa.star_phase2_partial(q, k[:, lo:], v[:, lo:], 2048 * 64, hi - lo, off)
+        torch.cuda.synchronize()
+        ra, rm, rl = oracle.partial(q.cpu(), k.cpu(), v.cpu(), lo, hi, off)
+        assert_out(a, ra, "A", max_abs=1e-5, mean_abs=1e-6)
+        assert_lse(m + torch.log(l), rm + np.log(rl), "partial LSE", rel=1e-6)
+
+
+# ----------------------------------------------------------------------------- merge
+@pytest.mark.parametrize("P,hq,rows,d", [(1, 4, 3, 128), (5, 8, 17, 128), (300, 32, 1, 128), (7, 2, 5, 64)])
+def test_softmax_merge(P, hq, rows, d):
+    rng = np.random.default_rng(P * 131 + rows)
+    a = rng.standard_normal((P, hq, rows, d)).astype(np.float32)
+    m = (rng.standard_normal((P, hq, rows)) * 20).astype(np.float32)
+    l = rng.uniform(0.5, 100.0, (P, hq, rows)).astype(np.float32)
+    if P > 1:   # some empty partitions and one row with every partition empty
+        m[0, 0, 0] = -np.inf
+        l[0, 0, 0] = 0.0
+        m[:, -1, -1] = -np.inf
+        l[:, -1, -1] = 0.0
+    ta, tm, tl = (torch.from_numpy(x).to(DEV) for x in (a, m, l))
+    o, lse = sa.star_softmax_merge(ta, tm, tl)
+    ob, _ = sa.star_softmax_merge(ta, tm, tl, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(a.astype(np.float64), m.astype(np.float64), l.astype(np.float64))
+    assert_out(o, ro, "O", max_abs=2e-5, mean_abs=2e-6)
+    assert_lse(lse, rl, "LSE", rel=1e-6)
+    assert_out(ob, ro, "O bf16", max_abs=2e-2, mean_abs=2e-3)
+
+
+def test_merge_needle_scale():
+    """Partials whose sums would overflow fp32 (scores near 90) merge exactly in log space."""
+    a = torch.tensor([[[[1.0] * 128]], [[[3.0] * 128]]], dtype=torch.float32, device=DEV)
+    m = torch.tensor([[[90.0]], [[90.0 + float(np.log(3.0))]]], dtype=torch.float32, device=DEV)
+    l = torch.ones((2, 1, 1), dtype=torch.float32, device=DEV)
+    o, lse = sa.star_softmax_merge(a, m, l)
+    torch.cuda.synchronize()
+    assert torch.allclose(o, torch.full_like(o, 2.5), atol=1e-5)
+    assert abs(float(lse) - (90.0 + np.log(4.0))) < 1e-4
+
+
+# ----------------------------------------------------------------------------- full Phase 2
+def _run_query_phase(cfg, x, bounds, k_tail, v_tail):
+    """S context partials + the query host's causal partial, merged (all through the C ABI)."""
+    q = x["q_qry"]
+    lq, L = cfg.lq, cfg.L
+    parts_a, parts_m, parts_l = [], [], []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        a, m, l = sa.star_phase2_partial(q, x["k_ctx"][:, lo:], x["v_ctx"][:, lo:], L * cfg.d, hi - lo, -1)
+        parts_a.append(a); parts_m.append(m); parts_l.append(l)
+    a, m, l = sa.star_phase2_partial(q, k_tail, v_tail, cfg.tail_cap * cfg.d, lq, 0)
+    parts_a.append(a); parts_m.append(m); parts_l.append(l)
+    return sa.star_softmax_merge(torch.stack(parts_a), torch.stack(parts_m), torch.stack(parts_l),
+                                 out_dtype=q.dtype)
+
+
+@pytest.mark.parametrize("hq,hkv,L,b,S,lq,T,dtype,d", [
+    (8, 2, 3000, 800, 3, 40, 3, "bf16", 128),
+    (16, 2, 1500, 512, 2, 20, 2, "bf16", 128),
+    (1, 1, 2048, 512, 2, 16, 4, "f32", 64),
+])
+def test_phase2_query_and_decode(hq, hkv, L, b, S, lq, T, dtype, d):
+    flush_print("phase2", hq, hkv, L, b, S, lq, T, dtype)
+    cfg = _cfg(hq, hkv, L, b, b, d=d, dtype=dtype, lq=lq, T=T, S=S, seed=23)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    x = {"k_ctx": k, "v_ctx": v}
+    x.update(sin.phase2_inputs(cfg, DEV))
+    bounds = shard_bounds(L, b, S)
+    tdt = x["k_qry"].dtype
+    k_tail = torch.zeros((hkv, cfg.tail_cap, d), dtype=tdt, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :lq] = x["k_qry"]
+    v_tail[:, :lq] = x["v_qry"]
+    o, lse = _run_query_phase(cfg, x, bounds, k_tail, v_tail)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase2_query(x["q_qry"].cpu(), k.cpu(), v.cpu(), bounds, x["k_qry"].cpu(), x["v_qry"].cpu())
+    tol = dict(max_abs=2e-2, mean_abs=2e-3) if dtype == "bf16" else dict(max_abs=1e-5, mean_abs=1e-6)
+    assert_out(o, ro, "query O", **tol)
+    assert_lse(lse, rl, "query LSE", rel=1e-5 if dtype == "bf16" else 1e-6)
+    ws = torch.empty(sa.star_decode_workspace_bytes(L, cfg.tail_cap, S, hq, hkv, d), dtype=torch.uint8, device=DEV)
+    for t in range(T):
+        od, ld = sa.star_decode_step(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k, v, bounds,
+                                     k_tail, v_tail, lq + t, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(k_tail[:, lq + t], x["k_dec"][t]) and torch.equal(v_tail[:, lq + t], x["v_dec"][t])
+        rod, rld = oracle.phase2_decode(x["q_dec"][t].cpu(), k.cpu(), v.cpu(), bounds, k_tail.cpu(),
+                                        v_tail.cpu(), lq + t + 1)
+        assert_out(od, rod, "decode O step %d" % t, **tol)
+        assert_lse(ld, rld, "decode LSE step %d" % t, rel=1e-5 if dtype == "bf16" else 1e-6)
+
+
+def test_decode_empty_shard_and_first_token():
+    """A shard with no tokens weighs nothing; tail_len = 0 is the first cached token."""
+    cfg = _cfg(8, 2, 1000, 250, 250, lq=1, T=1, S=4, seed=29)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    bounds = [0, 250, 250, 900, 1000]
+    k_tail = torch.zeros((2, 4, 128), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    o, lse = sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds, k_tail, v_tail, 0)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase2_decode(p2["q_dec"][0].cpu(), k.cpu(), v.cpu(), bounds, k_tail.cpu(), v_tail.cpu(), 1)
+    assert_out(o, ro, "O")
+    assert_lse(lse, rl, "LSE")
+
+
+def test_decode_shard_split_invariance():
+    """Any host split gives the same decode output (partition identity), to fp32 rounding."""
+    cfg = _cfg(8, 2, 4096, 1024, 1024, lq=8, T=1, S=4, seed=31)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    outs = []
+    for bounds in ([0, 4096], [0, 1024, 2048, 3072, 4096], [0, 1, 2, 4000, 4096], [0, 17, 1717, 4096]):
+        k_tail = torch.zeros((2, 9, 128), dtype=torch.bfloat16, device=DEV)
+        v_tail = torch.zeros_like(k_tail)
+        k_tail[:, :8] = p2["k_qry"]
+        v_tail[:, :8] = p2["v_qry"]
+        o, lse = sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds,
+                                     k_tail, v_tail, 8)
+        outs.append((o.float(), lse))
+    torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert (o - outs[0][0]).abs().max().item() <= 1e-2
+        assert (lse - outs[0][1]).abs().max().item() <= 1e-5 * max(1.0, outs[0][1].abs().max().item())
