@@ -29,6 +29,8 @@ struct AttnMfmaArgs {
 };
 
 bool attn_mfma_supported(int d, int hq, int hkv);
+// Largest per-kv-head token count the MFMA kernel addresses with 32-bit offsets.
+int64_t attn_mfma_max_tokens();
 
 hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               uint16_t* o, float* lse, int64_t L, int64_t block, int64_t anchor,

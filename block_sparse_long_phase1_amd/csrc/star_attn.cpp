@@ -100,6 +100,9 @@ star_status_t star_phase1_encode(const void* q, const void* k, const void* v, vo
             return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
         hipError_t e;
         if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
+            if (L > star::attn_mfma_max_tokens())
+                return fail(STAR_ERR_UNSUPPORTED, "L (%lld) above %lld tokens per kv head", (long long)L,
+                            (long long)star::attn_mfma_max_tokens());
             e = star::launch_phase1_mfma(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
                                          L, block, anchor, hq, hkv, scale, stream);
@@ -150,6 +153,9 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
             return fail(STAR_ERR_INVALID_ARG, "pointers and the kv head stride must be 16-byte aligned");
         hipError_t e;
         if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
+            if (n_kv > star::attn_mfma_max_tokens())
+                return fail(STAR_ERR_UNSUPPORTED, "n_kv (%lld) above %lld tokens per partition", (long long)n_kv,
+                            (long long)star::attn_mfma_max_tokens());
             int nrt, ns;
             int64_t split_len;
             star::partial_mfma_plan(rows, n_kv, hq, hkv, &nrt, &ns, &split_len);
