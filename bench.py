@@ -127,8 +127,7 @@ def main():
                for lo, hi in zip(bounds[:-1], bounds[1:]))
     ws_p = max(ws_p, sa.star_phase2_workspace_bytes(cfg.lq, cfg.lq, cfg.hq, cfg.hkv, cfg.d))
     ws_part = torch.empty(max(ws_p, 16), dtype=torch.uint8, device=dev)
-    ws_dec = torch.empty(max(16, sa.star_decode_workspace_bytes(cfg.L, cfg.tail_cap, S, cfg.hq, cfg.hkv, cfg.d)),
-                         dtype=torch.uint8, device=dev)
+    ws_dec = sa.decode_workspace(cfg.L, cfg.tail_cap, S, cfg.hq, cfg.hkv, cfg.d, dev)
     oq = torch.empty((cfg.hq, cfg.lq, cfg.d), dtype=dt, device=dev)
     lq_lse = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device=dev)
     od = torch.empty((cfg.decode_steps, cfg.hq, cfg.d), dtype=dt, device=dev)

@@ -220,6 +220,13 @@ def star_decode_workspace_bytes(L: int, tail_cap: int, n_shards: int, hq: int, h
     return int(load_library().star_decode_workspace_bytes(L, tail_cap, n_shards, hq, hkv, d))
 
 
+def decode_workspace(L: int, tail_cap: int, n_shards: int, hq: int, hkv: int, d: int, device):
+    """A zero-filled decode workspace (reusable across steps on one stream)."""
+    torch = _torch()
+    need = star_decode_workspace_bytes(L, tail_cap, n_shards, hq, hkv, d)
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
+
+
 def star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, tail_len: int,
                      o=None, lse=None, workspace=None, scale=None, want_lse: bool = True, stream=None):
     """One generated token: q_new [Hq,d], k_new/v_new [Hkv,d]; caches [Hkv,L,d] and
@@ -234,8 +241,7 @@ def star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, 
     if lse is None and want_lse:
         lse = torch.empty((hq,), dtype=torch.float32, device=q_new.device)
     if workspace is None:
-        need = star_decode_workspace_bytes(L, tail_cap, n_shards, hq, hkv, d)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_new.device)
+        workspace = decode_workspace(L, tail_cap, n_shards, hq, hkv, d, q_new.device)
     b = (ctypes.c_int64 * (n_shards + 1))(*[int(x) for x in bounds])
     st = load_library().star_decode_step(
         _dev(q_new, "q_new"), _same(k_new, q_new, "k_new", (hkv, d)), _same(v_new, q_new, "v_new", (hkv, d)),
@@ -251,5 +257,5 @@ def star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, 
 __all__ = [
     "CONFIGS", "StarConfig", "n_blocks", "shard_bounds", "load_library", "StarError",
     "star_phase1_encode", "star_phase2_workspace_bytes", "star_phase2_partial", "star_softmax_merge",
-    "star_decode_workspace_bytes", "star_decode_step", "STAR_F32", "STAR_BF16",
+    "star_decode_workspace_bytes", "star_decode_step", "decode_workspace", "STAR_F32", "STAR_BF16",
 ]

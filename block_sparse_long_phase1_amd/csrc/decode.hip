@@ -2,25 +2,27 @@
 //
 // "Star Attention: Efficient LLM Inference over Long Sequences"
 // (paper-graph-ui summary), section 3.4, Phase 2: each context host computes
-// the new token's local attention over its cached keys (Step 3) and the query
-// host does the same over its own growing cache (Steps 3 and 7); the partials
-// are merged in log space (Step 5, done by merge.hip).  Per generated token
+// the new token's local attention over its cached keys (Step 3), the query
+// host does the same over its own growing cache (Steps 3 and 7), and the
+// partial results are aggregated in log space (Step 5).  Per generated token
 // the work is linear in the cached length, so this kernel is a stream over the
-// K/V cache: every K/V byte is read exactly once per step for all G q heads of
-// its kv head.
+// K/V cache: every K/V byte is read once per step for all G q heads of its kv
+// head.
 //
 // Grid: (kv head, key chunk).  Chunks never straddle a host partition; the
 // query host's partition also holds the new token, read from k_new / v_new,
-// and the workgroup that owns it appends k_new / v_new to the tail cache (no
-// one reads that slot from memory in the same launch).
+// and the workgroup that owns it appends k_new / v_new to the query host's
+// cache (no one reads that slot from memory in the same launch).
 //
-// Each wave walks 64-key groups of its chunk.  Scores use MFMA
-// (v_mfma_f32_16x16x32_bf16, q heads of the group as the 16 rows, keys as the
-// 16 columns), fed straight from 16-byte global loads of K.  P.V is plain fp32
-// VALU work on 16-byte loads of V (lane = key quarter x 8-wide d slice), which
-// keeps every V load coalesced and needs no transpose.  Per-wave online softmax
-// state is combined across the 4 waves in LDS, and each workgroup writes one
-// normalised partial (A, m, l).
+// Each wave walks 32-key tiles of its chunk.  Both products run on
+// v_mfma_f32_32x32x16_bf16 with the G q heads as the 32-wide column block:
+// S^T = K Q^T takes K straight from 16-byte global loads, and O^T += V^T P^T
+// takes V^T from a wave-private LDS copy of the V tile (stored row-major,
+// read back with the transposing ds_read_b64_tr_b16).  Each wave keeps an
+// online softmax; the four waves are combined in LDS into one partial
+// (A, m, l) per chunk.  The last workgroup of a kv head to finish (an atomic
+// ticket in the workspace) merges that head's chunk partials in log space and
+// writes the output, then resets its ticket counter to zero.
 #include "common.h"
 #include "internal.h"
 
@@ -30,7 +32,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kD = 128;
-constexpr int kGroup = 64;   // keys per wave iteration
+constexpr int kT = 32;         // keys per tile
+constexpr int kVPitch = 144;   // bf16 per V row in LDS (288 B: 4 consecutive rows hit disjoint banks)
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 struct DecodeArgs {
     const uint16_t* q_new;
@@ -44,37 +48,35 @@ struct DecodeArgs {
     int hq, hkv, G;
     float sl2;
     DecodeChunkPlan plan;
-    float* pa;
+    float* pa;          // chunk partials: A [n_chunks][hq][d], m and l [n_chunks][hq]
     float* pm;
     float* pl;
+    unsigned* tickets;  // [hkv], zero between calls
+    uint16_t* o;        // [hq][d]
+    float* lse;         // [hq] or null
 };
 
-__device__ __forceinline__ float xor_max16(float x) {
-    x = fmaxf(x, __shfl_xor(x, 1));
-    x = fmaxf(x, __shfl_xor(x, 2));
-    x = fmaxf(x, __shfl_xor(x, 4));
-    x = fmaxf(x, __shfl_xor(x, 8));
-    return x;
-}
-__device__ __forceinline__ float xor_sum16(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
-    return x;
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// Four keys of one head-dim column from a row-major LDS tile (see the kernel comment).
+__device__ __forceinline__ u32x2v lds_read_tr(const uint16_t* p) {
+    lds_bf16x4* lp = (lds_bf16x4*)((__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(p)));
+    return __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 }  // namespace
 
 template <int G>
 __global__ void __launch_bounds__(kThreads, 2)
 decode_kernel(const DecodeArgs p) {
-    // Per-wave P exchange: [64 keys][G] probabilities + G rescale factors + G maxima.
-    __shared__ float p_lds[kWaves][kGroup * G];
-    __shared__ float alpha_lds[kWaves][G];
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[kWaves][kT * kVPitch];
     __shared__ float wm[kWaves][G], wl[kWaves][G];
-    __shared__ f32x4 wo[kWaves][G][kD / 4];
+    __shared__ float wo[kWaves][G][kD];
+    __shared__ unsigned ticket_sh;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, col = lane & 31;
     const int g = blockIdx.x % p.hkv;
     const int c = blockIdx.x / p.hkv;
     const DecodeChunkPlan& pl = p.plan;
@@ -91,9 +93,9 @@ decode_kernel(const DecodeArgs p) {
         kb = p.k_ctx + (int64_t)g * p.L * kD;
         vb = p.v_ctx + (int64_t)g * p.L * kD;
     } else {
-        int64_t tc = c - pl.chunk_prefix[pl.n_shards];
+        const int64_t tc = c - pl.chunk_prefix[pl.n_shards];
         lo = tc * pl.chunk;
-        int64_t n_tail = p.tail_len + 1;
+        const int64_t n_tail = p.tail_len + 1;
         hi = lo + pl.chunk < n_tail ? lo + pl.chunk : n_tail;
         kb = p.k_tail + (int64_t)g * p.tail_cap * kD;
         vb = p.v_tail + (int64_t)g * p.tail_cap * kD;
@@ -102,7 +104,8 @@ decode_kernel(const DecodeArgs p) {
             // Append the new token's k / v to the query host's cache (32 lanes x 16 B).
             if (tid < 32) {
                 const uint16_t* src = (tid < 16 ? p.k_new : p.v_new) + (int64_t)g * kD + (tid & 15) * 8;
-                uint16_t* dst = (tid < 16 ? p.k_tail : p.v_tail) + ((int64_t)g * p.tail_cap + p.tail_len) * kD + (tid & 15) * 8;
+                uint16_t* dst = (tid < 16 ? p.k_tail : p.v_tail) + ((int64_t)g * p.tail_cap + p.tail_len) * kD +
+                                (tid & 15) * 8;
                 *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
             }
         }
@@ -110,211 +113,271 @@ decode_kernel(const DecodeArgs p) {
     const uint16_t* knew = p.k_new + (int64_t)g * kD;
     const uint16_t* vnew = p.v_new + (int64_t)g * kD;
 
-    // ---- Q as the MFMA A operand: row m = lane % 16 (q head g*G + m), 8 d per slot group
-    const int qm = lane & 15, qk = lane >> 4;
-    bf16x8 qa[4];
+    // ---- Q^T as the B operand: column col = q head g*G + col (zero past G)
+    bf16x8 qb[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int st = 0; st < 8; ++st) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (qm < G) w = *reinterpret_cast<const u32x4*>(p.q_new + (int64_t)(g * G + qm) * kD + s * 32 + qk * 8);
-        qa[s] = __builtin_bit_cast(bf16x8, w);
+        if (col < G) w = *reinterpret_cast<const u32x4*>(p.q_new + (int64_t)(g * G + col) * kD + st * 16 + half * 8);
+        qb[st] = __builtin_bit_cast(bf16x8, w);
     }
 
-    // Running state.  S-layout lanes (lane/16 = query quad) track m for queries 4*(lane/16)+r;
-    // every lane accumulates O for all G queries over its d slice (lane % 16) and key quarter.
-    float m_run[4] = {kNoMax, kNoMax, kNoMax, kNoMax};
-    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
-    float o_acc[G][8];
+    f32x16 acc[4];
 #pragma unroll
-    for (int q = 0; q < G; ++q)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o_acc[q][e] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float mref = kNoMax, lsum = 0.f;
+    const float sl2 = p.sl2;
+    uint16_t* vt = vlds[wave];
+    // transposing-read addressing inside a 16-key step (see the P.V comment below)
+    const int trow = 4 * half + ((lane & 15) >> 2);
+    const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 
-    const int n_groups = (int)((hi - lo + kGroup - 1) / kGroup);
-    for (int gi = wave; gi < n_groups; gi += kWaves) {
-        const int64_t k0 = lo + (int64_t)gi * kGroup;
-        // K loads in MFMA B layout: sub-tile t, k-step s -> key k0+16t+lane%16, d 32s+8(lane/16)
-        u32x4 kr[4][4];
+    const int n_tiles = (int)((hi - lo + kT - 1) / kT);
+    // K rows as the A operand (row = key k0 + col) and V row-major pieces for LDS, for the
+    // tile that starts at key k0.  Keys past the chunk are clamped to its last key.
+    u32x4 ka[8], vr[8];
+    auto load_tile = [&](int64_t k0) {
+        int64_t key = k0 + col;
+        key = key < hi ? key : hi - 1;
+        const uint16_t* src = key == new_key ? knew : kb + key * kD;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            int64_t key = k0 + 16 * t + (lane & 15);
-            key = key < hi ? key : hi - 1;
-            const uint16_t* src = key == new_key ? knew : kb + key * kD;
+        for (int st = 0; st < 8; ++st) ka[st] = *reinterpret_cast<const u32x4*>(src + st * 16 + half * 8);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kr[t][s] = *reinterpret_cast<const u32x4*>(src + s * 32 + qk * 8);
+        for (int i = 0; i < 8; ++i) {
+            const int cc = lane + 64 * i;
+            int64_t vkey = k0 + (cc >> 4);
+            vkey = vkey < hi ? vkey : hi - 1;
+            const uint16_t* vsrc = vkey == new_key ? vnew : vb + vkey * kD;
+            vr[i] = *reinterpret_cast<const u32x4*>(vsrc + (cc & 15) * 8);
         }
-        // V loads: j -> key k0 + 4j + lane/16, d slice 8*(lane%16)
-        u32x4 vr[16];
+    };
+    if (wave < n_tiles) load_tile(lo + (int64_t)wave * kT);
+    for (int t = wave; t < n_tiles; t += kWaves) {
+        const int64_t k0 = lo + (int64_t)t * kT;
+        // S^T = K Q^T, and this tile's V into the wave's LDS tile
+        f32x16 s;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            int64_t key = k0 + 4 * j + (lane >> 4);
-            key = key < hi ? key : hi - 1;
-            const uint16_t* src = key == new_key ? vnew : vb + key * kD;
-            vr[j] = *reinterpret_cast<const u32x4*>(src + (lane & 15) * 8);
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int cc = lane + 64 * i;
+            *reinterpret_cast<u32x4*>(vt + (cc >> 4) * kVPitch + (cc & 15) * 8) = vr[i];
         }
-
-        // S = Q K^T for 4 sub-tiles of 16 keys
-        f32x4 sc[4];
+        // The operand registers are free again: the next tile's loads fly while this
+        // tile's softmax and P.V run.
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + kWaves < n_tiles) load_tile(k0 + (int64_t)kWaves * kT);
+        __builtin_amdgcn_sched_barrier(0);
+        // mask keys past the chunk (score rows: key k0 + 8*(r/4) + 4*half + r%4)
+        if (k0 + kT > hi) {
+            const int lim = (int)(hi - k0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, kr[t][s]), sc[t], 0, 0, 0);
+            for (int r = 0; r < 16; ++r)
+                if ((r >> 2) * 8 + half * 4 + (r & 3) >= lim) s[r] = -INFINITY;
         }
-        // scale to log2 units and mask keys past the chunk
-        float gmax[4];
+        // online softmax with a lazily moved reference
+        float mx = s[0];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gmax[r] = -INFINITY;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = half_pair_max(mx) * sl2;
+        if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleThreshold)) {
+            const float nref = fmaxf(mref, mx);
+            const float alpha = fast_exp2(mref - nref);
+            mref = nref;
+            lsum *= alpha;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool valid = k0 + 16 * t + (lane & 15) < hi;
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = valid ? sc[t][r] * p.sl2 : -INFINITY;
-                sc[t][r] = x;
-                gmax[r] = fmaxf(gmax[r], x);
-            }
+                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
         }
-        float alpha[4];
+        bf16x8 pb[2];
+        {
+            const float negm = -mref;
+            float ls = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float mnew = fmaxf(m_run[r], xor_max16(gmax[r]));
-            alpha[r] = fast_exp2(m_run[r] - mnew);
-            m_run[r] = mnew;
-            l_part[r] *= alpha[r];
-        }
-        // probabilities to LDS: p_lds[key][query]
-        const int qq = 4 * (lane >> 4);
-        if (qq < G) {
+            for (int u = 0; u < 2; ++u) {
+                float e[8];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4 pv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float e = fast_exp2(sc[t][r] - m_run[r]);
-                    pv[r] = e;
-                    l_part[r] += e;
+                for (int i = 0; i < 8; ++i) {
+                    e[i] = fast_exp2(fmaf(s[8 * u + i], sl2, negm));
+                    ls += e[i];
                 }
-                if (G >= 4) {
-                    *reinterpret_cast<f32x4*>(&p_lds[wave][(16 * t + (lane & 15)) * G + qq]) = pv;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < G; ++r) p_lds[wave][(16 * t + (lane & 15)) * G + r] = pv[r];
-                }
+                u32x4 w;
+                w[0] = pack_bf16x2(e[0], e[1]);
+                w[1] = pack_bf16x2(e[2], e[3]);
+                w[2] = pack_bf16x2(e[4], e[5]);
+                w[3] = pack_bf16x2(e[6], e[7]);
+                pb[u] = __builtin_bit_cast(bf16x8, w);
             }
-            if ((lane & 15) == 0) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (qq + r < G) alpha_lds[wave][qq + r] = alpha[r];
-            }
+            lsum += ls;
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // rescale O and accumulate P.V
+        // O^T += V^T P^T.  16-key step u: slot i of lane half h is key 16u + 8*(i/4) + 4h + i%4,
+        // the S^T accumulator layout.  In each 16-lane group of a transposing read, source lane
+        // s points at key (s/4) of its four-key set, columns 4*(s%4) .. +3 of the group's
+        // 16-wide head-dim slice; result lane i then holds column (i) of that slice for the
+        // four keys.  Two reads give the 8 slots: keys 16u + 4h + {0..3} and 16u + 8 + 4h + {0..3}.
 #pragma unroll
-        for (int q = 0; q < G; ++q) {
-            float al = alpha_lds[wave][q];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o_acc[q][e] *= al;
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int key = 4 * j + (lane >> 4);
-            float vf[8];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                vf[2 * w] = bf16_lo(vr[j][w]);
-                vf[2 * w + 1] = bf16_hi(vr[j][w]);
+            for (int db = 0; db < 4; ++db) {
+                const uint16_t* base = vt + (16 * u + trow) * kVPitch + db * 32 + tcol;
+                const u32x2v a0 = lds_read_tr(base);
+                const u32x2v a1 = lds_read_tr(base + 8 * kVPitch);
+                const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[u], acc[db], 0, 0, 0);
             }
-#pragma unroll
-            for (int q = 0; q < G; ++q) {
-                float pq = p_lds[wave][key * G + q];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o_acc[q][e] = fmaf(pq, vf[e], o_acc[q][e]);
-            }
-        }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // ---- reduce inside the wave: O over the 4 key quarters, l over the 16 key lanes
-#pragma unroll
-    for (int q = 0; q < G; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = o_acc[q][e];
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            o_acc[q][e] = x;
+    // ---- combine the four waves into this chunk's partial
+    const float lw = half_pair_sum(lsum);
+    if (col < G) {
+        if (half == 0) {
+            wm[wave][col] = mref;
+            wl[wave][col] = lw;
         }
-    float lw[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lw[r] = xor_sum16(l_part[r]);
-    if ((lane & 15) == 0) {
-        const int qq = 4 * (lane >> 4);
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (qq + r < G) {
-                wm[wave][qq + r] = m_run[r];
-                wl[wave][qq + r] = lw[r];
-            }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            wo[wave][q][2 * lane] = f32x4{o_acc[q][0], o_acc[q][1], o_acc[q][2], o_acc[q][3]};
-            wo[wave][q][2 * lane + 1] = f32x4{o_acc[q][4], o_acc[q][5], o_acc[q][6], o_acc[q][7]};
-        }
+            for (int r = 0; r < 16; ++r) wo[wave][col][db * 32 + (r >> 2) * 8 + half * 4 + (r & 3)] = acc[db][r];
     }
     __syncthreads();
-
-    // ---- combine the 4 waves and write this chunk's partial for each q head
-    for (int idx = tid; idx < G * (kD / 4); idx += kThreads) {
-        const int q = idx / (kD / 4), e4 = idx % (kD / 4);
+    for (int idx = tid; idx < G * kD; idx += kThreads) {
+        const int q = idx / kD, d = idx % kD;
         float M = wm[0][q];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][q]);
-        float W = 0.f;
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        float W = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            float sc = fast_exp2(wm[w][q] - M);
+            const float sc = fast_exp2(wm[w][q] - M);
             W += wl[w][q] * sc;
-            o += sc * wo[w][q][e4];
+            o += sc * wo[w][q][d];
         }
-        const float inv = W > 0.f ? 1.0f / W : 0.f;
         const int64_t prow = (int64_t)c * p.hq + g * G + q;
-        *reinterpret_cast<f32x4*>(p.pa + prow * kD + e4 * 4) = o * inv;
-        if (e4 == 0) {
-            p.pm[prow] = W > 0.f ? M * kLn2 : -INFINITY;
-            p.pl[prow] = W > 0.f ? W : 0.f;
+        // Device-scope stores: they complete at the level that every XCD reads.
+        __hip_atomic_store(p.pa + prow * kD + d, W > 0.f ? o / W : 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+            __hip_atomic_store(p.pm + prow, W > 0.f ? M * kLn2 : -INFINITY, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.pl + prow, W > 0.f ? W : 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+
+    // ---- the last chunk of this kv head to finish merges all of them.
+    // The partial was written with device-scope stores, so once they have completed
+    // (vmcnt 0) every workgroup can see it.  A device-scope release fence would add a
+    // write-back of this XCD's whole L2 per workgroup, which costs more than the merge.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) ticket_sh = __hip_atomic_fetch_add(&p.tickets[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket_sh != (unsigned)(pl.n_chunks - 1)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale cached partials below
+    const int nc = pl.n_chunks;
+    // One wave per q head, in one pass: lane = (chunk group cg of 16) x (head-dim slice ds
+    // of 32 columns).  Each lane folds chunks cg, cg + 16, ... into a running (m, w, o),
+    // then the 16 chunk groups are folded pairwise across lanes.
+    const int cg = lane >> 2, ds = lane & 3;
+    for (int q = wave; q < G; q += kWaves) {
+        const int h = g * G + q;
+        float rm = -INFINITY, rw = 0.f;
+        f32x4 o4[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int ci = cg; ci < nc; ci += 16) {
+            const int64_t row = (int64_t)ci * p.hq + h;
+            const float m = p.pm[row], l = p.pl[row];
+            const f32x4* src = reinterpret_cast<const f32x4*>(p.pa + row * kD + ds * 32);
+            const float nm = fmaxf(rm, m);
+            const float a = rm == -INFINITY ? 0.f : __expf(rm - nm);
+            const float b = m == -INFINITY ? 0.f : l * __expf(m - nm);
+            rw = rw * a + b;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o4[i] = o4[i] * a + b * src[i];
+            rm = nm;
+        }
+#pragma unroll
+        for (int sh = 4; sh < 64; sh <<= 1) {
+            const float om = __shfl_xor(rm, sh), ow = __shfl_xor(rw, sh);
+            const float nm = fmaxf(rm, om);
+            const float a = rm == -INFINITY ? 0.f : __expf(rm - nm);
+            const float b = om == -INFINITY ? 0.f : __expf(om - nm);
+            rw = rw * a + ow * b;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[i][e] = o4[i][e] * a + __shfl_xor(o4[i][e], sh) * b;
+            rm = nm;
+        }
+        const bool empty = rm == -INFINITY || !(rw > 0.f);
+        if (cg == 0) {
+            const float inv = empty ? 0.f : 1.0f / rw;
+            u32x4 w4[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                w4[i >> 1][(i & 1) * 2 + 0] = pack_bf16x2(o4[i][0] * inv, o4[i][1] * inv);
+                w4[i >> 1][(i & 1) * 2 + 1] = pack_bf16x2(o4[i][2] * inv, o4[i][3] * inv);
+            }
+            u32x4* dst = reinterpret_cast<u32x4*>(p.o + (int64_t)h * kD + ds * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = w4[i];
+            if (ds == 0 && p.lse) p.lse[h] = empty ? -INFINITY : rm + __logf(rw);
+        }
+    }
+    // ready for the next call on this stream
+    if (tid == 0) __hip_atomic_store(&p.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 bool decode_bf16_supported(int d, int hq, int hkv) {
     if (d != kD || hkv < 1 || hq % hkv) return false;
-    int G = hq / hkv;
-    return G == 1 || G == 2 || G == 4 || G == 8;
+    const int G = hq / hkv;
+    return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
 }
 
-int64_t decode_chunk_len(int64_t L, int64_t tail_cap, int32_t hkv) {
-    // About 2048 workgroups in total, chunks a multiple of the 4 x 64 keys a pass covers.
-    int64_t per_head = L + tail_cap;
-    int64_t want = (per_head * hkv + 2047) / 2048;
-    int64_t ch = 256;
-    while (ch < want && ch < 8192) ch <<= 1;
-    return ch;
+int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv) {
+    // About two resident workgroups per compute unit (256 CUs), all in one round: each kv
+    // head gets up to 440/hkv - 1 context chunks, spread over its shards by length, plus
+    // its query-host chunk(s).  Chunks are a multiple of the 4 x 32 keys one pass covers.
+    const int64_t L = shard_bounds[n_shards] - shard_bounds[0];
+    int64_t budget = 440 / hkv - 1;
+    if (budget < n_shards) budget = n_shards;
+    int64_t ch = 128;
+    for (int r = 0; r < n_shards; ++r) {
+        const int64_t len = shard_bounds[r + 1] - shard_bounds[r];
+        if (len <= 0) continue;
+        int64_t cr = budget * len / (L > 0 ? L : 1);
+        if (cr < 1) cr = 1;
+        const int64_t need = (len + cr - 1) / cr;
+        if (need > ch) ch = need;
+    }
+    return (ch + 127) / 128 * 128;
+}
+
+int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv) {
+    // The plan above gives each shard at most budget*len/L chunks (at least 1), hence at
+    // most budget + n_shards context chunks, and the query host at most ceil(tail_cap/128).
+    int64_t budget = 440 / hkv - 1;
+    if (budget < n_shards) budget = n_shards;
+    return budget + n_shards + (tail_cap + 127) / 128;
 }
 
 hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
                               const uint16_t* k_ctx, const uint16_t* v_ctx, int64_t L,
                               uint16_t* k_tail, uint16_t* v_tail, int64_t tail_len, int64_t tail_cap,
                               int hq, int hkv, float scale, const DecodeChunkPlan& plan,
-                              float* part_a, float* part_m, float* part_l, hipStream_t stream) {
+                              float* part_a, float* part_m, float* part_l, unsigned* tickets,
+                              uint16_t* o, float* lse, hipStream_t stream) {
     DecodeArgs a;
     a.q_new = q_new; a.k_new = k_new; a.v_new = v_new;
     a.k_ctx = k_ctx; a.v_ctx = v_ctx; a.k_tail = k_tail; a.v_tail = v_tail;
@@ -323,14 +386,17 @@ hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, cons
     a.sl2 = scale * kLog2e;
     a.plan = plan;
     a.pa = part_a; a.pm = part_m; a.pl = part_l;
+    a.tickets = tickets;
+    a.o = o; a.lse = lse;
     const int64_t grid = (int64_t)hkv * plan.n_chunks;
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    dim3 gd((unsigned)grid), bd(kThreads);
+    const dim3 gd((unsigned)grid), bd(kThreads);
     switch (a.G) {
         case 1: hipLaunchKernelGGL(decode_kernel<1>, gd, bd, 0, stream, a); break;
         case 2: hipLaunchKernelGGL(decode_kernel<2>, gd, bd, 0, stream, a); break;
         case 4: hipLaunchKernelGGL(decode_kernel<4>, gd, bd, 0, stream, a); break;
         case 8: hipLaunchKernelGGL(decode_kernel<8>, gd, bd, 0, stream, a); break;
+        case 16: hipLaunchKernelGGL(decode_kernel<16>, gd, bd, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

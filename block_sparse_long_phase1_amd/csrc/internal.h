@@ -50,8 +50,9 @@ hipError_t launch_merge(const float* a, const float* m, const float* l, int n_pa
                         int d, void* o, bool out_bf16, float* lse_out, float* m_out, float* l_out,
                         hipStream_t stream);
 
-// Split-KV decode (bf16, d = 128): chunk partials for every kv head, plus the append of
-// the new token into the query host's cache.
+// Split-KV decode (bf16, d = 128): chunk partials for every kv head, the append of the
+// new token into the query host's cache, and the log-space merge by the last chunk of
+// each kv head (tickets: hkv zero-initialised counters, left at zero).
 struct DecodeChunkPlan {
     int n_shards;
     int64_t chunk;                 // keys per chunk
@@ -61,12 +62,16 @@ struct DecodeChunkPlan {
 };
 
 bool decode_bf16_supported(int d, int hq, int hkv);
-int64_t decode_chunk_len(int64_t L, int64_t tail_cap, int32_t hkv);
+// Keys per decode chunk for a shard layout, and an upper bound on the chunk count of any
+// call with at most tail_cap query-host tokens and n_shards shards.
+int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv);
+int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv);
 hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
                               const uint16_t* k_ctx, const uint16_t* v_ctx, int64_t L,
                               uint16_t* k_tail, uint16_t* v_tail, int64_t tail_len, int64_t tail_cap,
                               int hq, int hkv, float scale, const DecodeChunkPlan& plan,
-                              float* part_a, float* part_m, float* part_l, hipStream_t stream);
+                              float* part_a, float* part_m, float* part_l, unsigned* tickets,
+                              uint16_t* o, float* lse, hipStream_t stream);
 
 // Plain vector path (fp32 or bf16 inputs, any d <= 256 with d % 4 == 0): one wave per row.
 struct RowKeySeg {

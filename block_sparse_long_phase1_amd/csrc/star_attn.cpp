@@ -220,10 +220,9 @@ star_status_t star_softmax_merge(const float* a, const float* m, const float* l,
 // ------------------------------------------------------------------------ decode
 size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards, int32_t hq,
                                    int32_t hkv, int32_t d) {
-    if (L < 1 || tail_cap < 1 || n_shards < 1 || hq < 1 || hkv < 1 || hq % hkv || d < 1) return 0;
-    const int64_t ch = star::decode_chunk_len(L, tail_cap, hkv);
-    const int64_t n_max = (L + ch - 1) / ch + n_shards + (tail_cap + ch - 1) / ch + 1;
-    return partials_bytes(n_max, hq, d);
+    if (L < 1 || tail_cap < 1 || n_shards < 1 || n_shards > 64 || hq < 1 || hkv < 1 || hq % hkv || d < 1)
+        return 0;
+    return partials_bytes(star::decode_max_chunks(tail_cap, n_shards, hkv), hq, d) + round_up((size_t)hkv * 4);
 }
 
 star_status_t star_decode_step(const void* q_new, const void* k_new, const void* v_new,
@@ -255,7 +254,7 @@ star_status_t star_decode_step(const void* q_new, const void* k_new, const void*
         if (dt == STAR_BF16 && star::decode_bf16_supported(d, hq, hkv)) {
             star::DecodeChunkPlan plan = {};
             plan.n_shards = n_shards;
-            plan.chunk = star::decode_chunk_len(L, tail_cap, hkv);
+            plan.chunk = star::decode_chunk_len(shard_bounds, n_shards, hkv);
             int64_t nc = 0;
             for (int r = 0; r < n_shards; ++r) {
                 plan.shard_lo[r] = shard_bounds[r];
@@ -267,20 +266,22 @@ star_status_t star_decode_step(const void* q_new, const void* k_new, const void*
             nc += (tail_len + 1 + plan.chunk - 1) / plan.chunk;
             plan.chunk_prefix[n_shards + 1] = (int32_t)nc;
             plan.n_chunks = (int32_t)nc;
-            const size_t need = partials_bytes(nc, hq, d);
+            const int64_t n_max = star::decode_max_chunks(tail_cap, n_shards, hkv);
+            if (nc > n_max) return fail(STAR_ERR_HIP, "star_decode_step: chunk plan exceeds its bound");
+            const size_t part_bytes = partials_bytes(n_max, hq, d);
+            const size_t need = part_bytes + round_up((size_t)hkv * 4);
             if (!workspace || workspace_bytes < need || !aligned16(workspace))
                 return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
                             workspace ? workspace_bytes : (size_t)0);
             float *wa, *wm, *wl;
-            partials_ptrs(workspace, nc, hq, d, &wa, &wm, &wl);
+            partials_ptrs(workspace, n_max, hq, d, &wa, &wm, &wl);
+            unsigned* tickets = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + part_bytes);
             e = star::launch_decode_bf16(static_cast<const uint16_t*>(q_new), static_cast<const uint16_t*>(k_new),
                                          static_cast<const uint16_t*>(v_new), static_cast<const uint16_t*>(k_ctx),
                                          static_cast<const uint16_t*>(v_ctx), L, static_cast<uint16_t*>(k_tail),
                                          static_cast<uint16_t*>(v_tail), tail_len, tail_cap, hq, hkv, scale, plan,
-                                         wa, wm, wl, stream);
+                                         wa, wm, wl, tickets, static_cast<uint16_t*>(o), lse, stream);
             if (e != hipSuccess) return hip_fail(e, "star_decode_step launch");
-            e = star::launch_merge(wa, wm, wl, (int)nc, hq, d, o, true, lse, nullptr, nullptr, stream);
-            if (e != hipSuccess) return hip_fail(e, "star_decode_step merge launch");
         } else {
             e = star::launch_tail_append(k_new, v_new, k_tail, v_tail, tail_len, tail_cap, hkv, d, elem_bytes(dt), stream);
             if (e != hipSuccess) return hip_fail(e, "star_decode_step append launch");

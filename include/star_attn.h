@@ -26,9 +26,9 @@
  *   multiple of 4).  Partials and LSEs are always fp32.
  * Memory and ownership.  Every pointer not marked "host" is device memory
  *   owned by the caller, 16-byte aligned.  The library never allocates or
- *   frees device memory and keeps no state between calls; entry points that
- *   need scratch take a caller-provided workspace whose size the matching
- *   *_workspace_bytes() call returns.
+ *   frees device memory and keeps no state between calls other than what a
+ *   caller-provided workspace holds; entry points that need scratch take such
+ *   a workspace, whose size the matching *_workspace_bytes() call returns.
  * Streams and errors.  Every call only enqueues work on `stream` and returns
  *   without synchronising.  Arguments are checked on the host before anything
  *   is enqueued: a bad argument returns STAR_ERR_INVALID_ARG, a shape the
@@ -161,8 +161,14 @@ star_status_t star_softmax_merge(const float *a, const float *m, const float *l,
  *                                           entry tail_len is written
  *   o [hq, d] (dt), lse [hq] fp32 or NULL
  *   workspace: star_decode_workspace_bytes(L, tail_cap, n_shards, hq, hkv, d)
+ *         bytes.  It must be zero-filled before its first use; every call that
+ *         completes leaves it ready for the next (its per-kv-head completion
+ *         counters back at zero).  Calls that share a workspace must be
+ *         ordered on one stream.
  *   0 <= tail_len < tail_cap.
- * Two kernel launches (chunk partials with the append, then the merge).
+ * bf16 with d = 128: one kernel launch (chunk partials, the append, and the
+ * merge done by the last chunk of each kv head).  Other shapes: an append
+ * launch and a vector-path launch.
  */
 size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards,
                                    int32_t hq, int32_t hkv, int32_t d);

@@ -93,8 +93,7 @@ def test_full_workload(name):
 
     # ---- Phase 2 decode, every step; oracle on the first and the last
     T = cfg.decode_steps
-    ws = torch.empty(sa.star_decode_workspace_bytes(cfg.L, cfg.tail_cap, cfg.shards, cfg.hq, cfg.hkv, cfg.d),
-                     dtype=torch.uint8, device=DEV)
+    ws = sa.decode_workspace(cfg.L, cfg.tail_cap, cfg.shards, cfg.hq, cfg.hkv, cfg.d, DEV)
     od = torch.empty((T, cfg.hq, cfg.d), dtype=q.dtype, device=DEV)
     ld = torch.empty((T, cfg.hq), dtype=torch.float32, device=DEV)
     for t in range(T):

@@ -205,7 +205,7 @@ def test_phase2_query_and_decode(hq, hkv, L, b, S, lq, T, dtype, d):
     tol = dict(max_abs=2e-2, mean_abs=2e-3) if dtype == "bf16" else dict(max_abs=1e-5, mean_abs=1e-6)
     assert_out(o, ro, "query O", **tol)
     assert_lse(lse, rl, "query LSE", rel=1e-5 if dtype == "bf16" else 1e-6)
-    ws = torch.empty(sa.star_decode_workspace_bytes(L, cfg.tail_cap, S, hq, hkv, d), dtype=torch.uint8, device=DEV)
+    ws = sa.decode_workspace(L, cfg.tail_cap, S, hq, hkv, d, DEV)
     for t in range(T):
         od, ld = sa.star_decode_step(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k, v, bounds,
                                      k_tail, v_tail, lq + t, workspace=ws)
