@@ -17,13 +17,14 @@
 // every lane owns one query column, so the softmax row statistics need no
 // cross-lane reduction beyond one exchange between lanes l and l^32.  The
 // probabilities P^T come out of the score accumulators already in the
-// B-operand layout of the second product O^T += V^T P^T; V is transposed once
-// per tile while it is written to LDS.
+// B-operand layout of the second product O^T += V^T P^T, whose V^T operand is
+// read from the row-major V tile with transposing LDS reads.
 //
-// Tiles of 64 keys are double-buffered in LDS; the global loads of tile j+1
-// are in flight while tile j is multiplied, and each phase reads all of its
-// MFMA operands from LDS before its first MFMA so the LDS latency is paid once
-// per phase.  Softmax runs in the exp2 domain with a lazily updated reference
+// Tiles of 64 keys are double-buffered in LDS and copied there by direct
+// global-to-LDS loads, which take no registers and no LDS store instructions;
+// the copy of tile j+1 is in flight while tile j is multiplied.  The two stages
+// are separate LDS objects so that reads of one never wait for the copy into
+// the other.  Softmax runs in the exp2 domain with a lazily updated reference
 // max: the accumulators are only rescaled when a row's max grows by more than
 // 2^8, which keeps every probability below 256 and is exact after the final
 // normalisation.
@@ -38,66 +39,52 @@ constexpr int kThreads = 512;
 constexpr int kBN = 64;          // keys per tile
 constexpr int kD = 128;          // head dim of this kernel
 constexpr int kQPB = 256;        // queries per workgroup
-constexpr int kStages = 2;
 constexpr int kKB = kBN / 32;    // 32-key MFMA blocks per tile
-constexpr int kLoads = kBN / 16; // 16-byte global loads per thread per tile
-constexpr int kKPitch = kD + 8;  // bf16 per K row in LDS (272 B: conflict-free 16 B reads)
-constexpr int kVPitch = kBN + 4; // bf16 per V^T row in LDS (136 B: conflict-free 8 B reads)
-constexpr int kKTile = kBN * kKPitch;
-constexpr int kVTile = kD * kVPitch;
-constexpr int kStage = kKTile + kVTile;       // bf16 elements per pipeline stage
+// LDS tile layout.  A tile's 64 key rows (256 B each) sit in 16 blocks of four rows,
+// block b holding rows b, b+16, b+32, b+48; consecutive rows therefore fall in
+// consecutive blocks.  Blocks are padded so that each starts 16 B (K) or 64 B (V)
+// further around the 256-byte bank cycle than the previous one: the 16 rows read by
+// a K operand read, and the 4 rows x 4 chunks of a transposing V read, then touch
+// distinct banks, and every operand address is one per-lane base plus a constant.
+constexpr int kKBlock = 1024 + 16;            // bytes per K block
+constexpr int kVBlock = 1024 + 64;            // bytes per V block
+constexpr int kKTileBytes = 16 * kKBlock;
+constexpr int kVTileBytes = 16 * kVBlock;
+constexpr int kStageBytes = kKTileBytes + kVTileBytes;
 constexpr float kRescaleThreshold = 8.0f;     // log2 units
 
-// Per-thread share of one tile in flight: threads 0..255 carry V (4 keys x 8 d,
-// transposed on the way into LDS), threads 256..511 carry K (four 16-byte
-// chunks of row-major K).
-struct TileSrc {
-    u32x4 r[kLoads];
-};
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
-// Issue the global loads of one tile.  Keys at or past `kmax` are clamped to
-// kmax-1 (always a valid row); their scores are masked later.  Key offsets from
-// the kv head's base fit in 32 bits (checked on the host).
-__device__ __forceinline__ void load_tile(TileSrc& t, const uint16_t* __restrict__ kb,
-                                          const uint16_t* __restrict__ vb, int key0, int kmax, int tid) {
-    if (tid < 256) {
-        const int kq = tid & 15, oct = tid >> 4;
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const int key = min(key0 + kq * kLoads + j, kmax - 1);
-            t.r[j] = *reinterpret_cast<const u32x4*>(vb + key * kD + oct * 8);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const int c = tid - 256 + 256 * j;
-            const int key = min(key0 + (c >> 4), kmax - 1);
-            t.r[j] = *reinterpret_cast<const u32x4*>(kb + key * kD + (c & 15) * 8);
-        }
-    }
+// Four keys of one head-dim column from a row-major LDS tile (see the P.V comment).
+__device__ __forceinline__ u32x2v lds_read_tr(const char* p) {
+    lds_bf16x4* lp = (lds_bf16x4*)((__attribute__((address_space(3))) char*)(const_cast<char*>(p)));
+    return __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
-// Write a loaded tile into one LDS stage: K row-major, V transposed (V^T[d][key]).
-__device__ __forceinline__ void store_tile(const TileSrc& t, uint16_t* __restrict__ stage, int tid) {
-    if (tid < 256) {
-        uint16_t* vs = stage + kKTile;
-        const int kq = tid & 15, oct = tid >> 4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy one K/V tile straight from global memory into an LDS stage (no registers).
+// One instruction fills one 1 KB block (lane i writes bytes 16i .. 16i+15 of it):
+// row b + 16*(i/16), 16-byte chunk i%16.  Waves 0-3 fill the K blocks, waves 4-7 the
+// V blocks, four each.  Keys at or past `kmax` are clamped to kmax-1 (always a valid
+// row); their scores are masked later.  Key offsets from the kv head's base fit in
+// 32 bits (checked on the host).  `wave` must be wave-uniform.
+__device__ __forceinline__ void dma_tile(char* stage, const uint16_t* __restrict__ kb,
+                                         const uint16_t* __restrict__ vb, int key0, int kmax, int wave, int lane) {
+    const bool is_k = wave < 4;
+    const char* src = reinterpret_cast<const char*>(is_k ? kb : vb);
+    char* dst = stage + (is_k ? 0 : kKTileBytes);
+    const int blk_bytes = is_k ? kKBlock : kVBlock;
+    const int w4 = wave & 3;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {  // word w of each key row holds d = 8*oct + 2w, +1
-            const int d = oct * 8 + 2 * w;
-#pragma unroll
-            for (int jp = 0; jp < kLoads; jp += 2) {
-                *reinterpret_cast<uint32_t*>(vs + d * kVPitch + kq * kLoads + jp) = pack_lo16(t.r[jp][w], t.r[jp + 1][w]);
-                *reinterpret_cast<uint32_t*>(vs + (d + 1) * kVPitch + kq * kLoads + jp) =
-                    pack_hi16(t.r[jp][w], t.r[jp + 1][w]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const int c = tid - 256 + 256 * j;
-            *reinterpret_cast<u32x4*>(stage + (c >> 4) * kKPitch + (c & 15) * 8) = t.r[j];
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int b = w4 * 4 + i;
+        const int row = b + 16 * (lane >> 4);
+        const int key = min(key0 + row, kmax - 1);
+        const uint32_t off = (uint32_t)key * (kD * 2) + (uint32_t)(lane & 15) * 16u;
+        __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_void*)(dst + b * blk_bytes), 16, 0, 0);
     }
 }
 
@@ -118,7 +105,8 @@ struct KeyPlan {
 template <int MODE>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_mfma_kernel(const AttnMfmaArgs p) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kStages * kStage];
+    __shared__ __attribute__((aligned(16))) char smem0[kStageBytes];
+    __shared__ __attribute__((aligned(16))) char smem1[kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -214,7 +202,6 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     const int kmax = (int)kp.kmax;
     const int a_lo = (int)kp.a_lo, b_lo = (int)kp.b_lo;
     auto tile_key0 = [&](int j) -> int { return j < kp.nta ? a_lo + j * kBN : b_lo + (j - kp.nta) * kBN; };
-    auto stage_of = [&](int j) -> uint16_t* { return smem + (j % kStages) * kStage; };
 
     f32x16 s[kKB];   // S^T of the current tile, one 32-key block per entry
 
@@ -239,98 +226,115 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         }
     };
 
-    if (nt > 0) {
-        TileSrc src;
-        load_tile(src, kbase, vbase, tile_key0(0), kmax, tid);
-        store_tile(src, stage_of(0), tid);
-        __syncthreads();
+    // transposing-read addressing inside a 16-key step (see the P.V comment below)
+    const int trow = 4 * half + ((lane & 15) >> 2);
+    const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 
-        for (int j = 0; j < nt; ++j) {
-            if (j + 1 < nt) load_tile(src, kbase, vbase, tile_key0(j + 1), kmax, tid);
-            const uint16_t* ks = stage_of(j);
-            const uint16_t* vs = ks + kKTile;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    auto step = [&](int j, const char* cur, char* nxt) {
+        if (j + 1 < nt) dma_tile(nxt, kbase, vbase, tile_key0(j + 1), kmax, uwave, lane);
+        const char* vs = cur + kKTileBytes;
+        // K operand: row kb*32 + col, chunk 2*st + half.  Rows col and col+16 differ by 256 B
+        // inside a block; kb adds two rows per block (512 B).
+        const char* kp = cur + (col & 15) * kKBlock + (col >> 4) * 256 + half * 16;
+        // V operand rows 16u + trow (+8): block trow (+8), row u inside it.
+        const char* vp = vs + trow * kVBlock + tcol * 2;
 
-            // ---- S^T = K Q^T, one 32-key block at a time, all eight K operands read first
+        // ---- S^T = K Q^T, one 32-key block at a time, all eight K operands read first
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb) {
-                u32x4 ka[8];
+        for (int kb = 0; kb < kKB; ++kb) {
+            u32x4 ka[8];
 #pragma unroll
-                for (int st = 0; st < 8; ++st)
-                    ka[st] = *reinterpret_cast<const u32x4*>(ks + (kb * 32 + col) * kKPitch + st * 16 + half * 8);
+            for (int st = 0; st < 8; ++st)
+                ka[st] = *reinterpret_cast<const u32x4*>(kp + kb * 512 + st * 32);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-                for (int st = 0; st < 8; ++st)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s[kb],
-                                                                   0, 0, 0);
-            }
-            mask(j);
+            for (int st = 0; st < 8; ++st)
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s[kb],
+                                                               0, 0, 0);
+        }
+        mask(j);
 
-            // ---- tile max; move the reference (and rescale) only if it grew past 2^8
-            {
-                float mx = s[0][0];
+        // ---- tile max; move the reference (and rescale) only if it grew past 2^8
+        {
+            float mx = s[0][0];
 #pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
+            for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-                mx = half_pair_max(mx) * sl2;
-                mtrue = fmaxf(mtrue, mx);
-                if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleThreshold)) {
-                    const float nref = fmaxf(mref, mx);
-                    const float alpha = fast_exp2(mref - nref);
-                    mref = nref;
-                    lsum *= alpha;
-#pragma unroll
-                    for (int db = 0; db < 4; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-                }
-            }
-
-            // ---- V^T operands (16-key step u: slot i of lane half h is key
-            //      16u + 8*(i/4) + 4h + i%4 of the tile, matching the S^T layout)
-            u32x4 va[2 * kKB][4];
-#pragma unroll
-            for (int u = 0; u < 2 * kKB; ++u)
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const uint16_t* vp = vs + (db * 32 + col) * kVPitch + u * 16 + half * 4;
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-                    va[u][db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                }
-
-            // ---- P^T = exp2(S^T - ref) in place, row sums from the unrounded values
-            {
-                const float negm = -mref;
-                float ls = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        s[kb][r] = fast_exp2(fmaf(s[kb][r], sl2, negm));
-                        ls += s[kb][r];
-                    }
-                lsum += ls;
-            }
-
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int u = 0; u < 2 * kKB; ++u) {
-                u32x4 w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = pack_bf16x2(s[u >> 1][8 * (u & 1) + 2 * i], s[u >> 1][8 * (u & 1) + 2 * i + 1]);
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = half_pair_max(mx) * sl2;
+            mtrue = fmaxf(mtrue, mx);
+            if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleThreshold)) {
+                const float nref = fmaxf(mref, mx);
+                const float alpha = fast_exp2(mref - nref);
+                mref = nref;
+                lsum *= alpha;
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[u][db]), pb,
-                                                                     acc[db], 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            }
+        }
+
+        // ---- V^T operands by transposing reads of the row-major V tile.  16-key step u:
+        //      slot i of lane half h is key 16u + 8*(i/4) + 4h + i%4, the S^T layout.  In a
+        //      16-lane group, source lane s points at key (s/4) of a four-key set and at
+        //      columns 4*(s%4) .. +3 of the group's 16-wide head-dim slice; result lane i
+        //      holds column i of that slice for the four keys.
+        u32x4 va[2 * kKB][4];
+#pragma unroll
+        for (int u = 0; u < 2 * kKB; ++u)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const u32x2v a0 = lds_read_tr(vp + u * 256 + db * 64);
+                const u32x2v a1 = lds_read_tr(vp + 8 * kVBlock + u * 256 + db * 64);
+                va[u][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
             }
 
-            if (j + 1 < nt) store_tile(src, stage_of(j + 1), tid);
-            __syncthreads();
+        // ---- P^T = exp2(S^T - ref) in place, row sums from the unrounded values
+        {
+            const float negm = -mref;
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] = fast_exp2(fmaf(s[kb][r], sl2, negm));
+                    ls += s[kb][r];
+                }
+            lsum += ls;
         }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int u = 0; u < 2 * kKB; ++u) {
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = pack_bf16x2(s[u >> 1][8 * (u & 1) + 2 * i], s[u >> 1][8 * (u & 1) + 2 * i + 1]);
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[u][db]), pb,
+                                                                 acc[db], 0, 0, 0);
+        }
+        // This wave's copies into `nxt` have landed; after the barrier every wave's have,
+        // and every wave is done reading `cur`.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    if (nt > 0) {
+        dma_tile(smem0, kbase, vbase, tile_key0(0), kmax, uwave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        int j = 0;
+        for (; j + 1 < nt; j += 2) {
+            step(j, smem0, smem1);
+            step(j + 1, smem1, smem0);
+        }
+        if (j < nt) step(j, smem0, smem1);
     }
 
     // ---------------------------------------------------------------- epilogue
