@@ -3,8 +3,8 @@
 One step = one pass of the whole path over one batch of synthetic input, inputs already
 resident in HBM:
   Phase 1  star_phase1_encode over the whole context (one kernel launch),
-  Phase 2  query encoding: one star_phase2_partial per context shard, one for the query
-           host's own cache, then star_softmax_merge,
+  Phase 2  query encoding: star_phase2_query (the partials of every context shard and of
+           the query host's own cache, then their merge),
            then decode_steps x star_decode_step (append + split-KV partials + merge).
 
 Prints ONE JSON line.  `value` is context tokens per second of the whole step
@@ -119,14 +119,8 @@ def main():
     k_tail[:, :cfg.lq] = x["k_qry"]
     v_tail[:, :cfg.lq] = x["v_qry"]
     S = len(bounds) - 1
-    P = S + 1
-    pa = torch.empty((P, cfg.hq, cfg.lq, cfg.d), dtype=torch.float32, device=dev)
-    pm = torch.empty((P, cfg.hq, cfg.lq), dtype=torch.float32, device=dev)
-    pl = torch.empty_like(pm)
-    ws_p = max(sa.star_phase2_workspace_bytes(cfg.lq, hi - lo, cfg.hq, cfg.hkv, cfg.d)
-               for lo, hi in zip(bounds[:-1], bounds[1:]))
-    ws_p = max(ws_p, sa.star_phase2_workspace_bytes(cfg.lq, cfg.lq, cfg.hq, cfg.hkv, cfg.d))
-    ws_part = torch.empty(max(ws_p, 16), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(max(sa.star_phase2_query_workspace_bytes(cfg.lq, S, cfg.hq, cfg.hkv, cfg.d), 16),
+                       dtype=torch.uint8, device=dev)
     ws_dec = sa.decode_workspace(cfg.L, cfg.tail_cap, S, cfg.hq, cfg.hkv, cfg.d, dev)
     oq = torch.empty((cfg.hq, cfg.lq, cfg.d), dtype=dt, device=dev)
     lq_lse = torch.empty((cfg.hq, cfg.lq), dtype=torch.float32, device=dev)
@@ -138,12 +132,8 @@ def main():
         sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor, o=o, lse=lse, stream=stream)
 
     def query_phase():
-        for r, (lo, hi) in enumerate(zip(bounds[:-1], bounds[1:])):
-            sa.star_phase2_partial(x["q_qry"], k[:, lo:], v[:, lo:], cfg.L * cfg.d, hi - lo, -1,
-                                   a_out=pa[r], m_out=pm[r], l_out=pl[r], workspace=ws_part, stream=stream)
-        sa.star_phase2_partial(x["q_qry"], k_tail, v_tail, cfg.tail_cap * cfg.d, cfg.lq, 0,
-                               a_out=pa[S], m_out=pm[S], l_out=pl[S], workspace=ws_part, stream=stream)
-        sa.star_softmax_merge(pa, pm, pl, o=oq, lse=lq_lse, stream=stream)
+        sa.star_phase2_query(x["q_qry"], k, v, bounds, k_tail, v_tail, cfg.lq, o=oq, lse=lq_lse,
+                             workspace=ws_q, stream=stream)
 
     def decode(t):
         sa.star_decode_step(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k, v, bounds, k_tail, v_tail,

@@ -61,6 +61,11 @@ def load_library(path: str | None = None):
         lib.star_phase2_partial.restype = ctypes.c_int
         lib.star_softmax_merge.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, ctypes.c_int, vp, vp]
         lib.star_softmax_merge.restype = ctypes.c_int
+        lib.star_phase2_query_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.star_phase2_query_workspace_bytes.restype = sz
+        lib.star_phase2_query.argtypes = [vp, i32, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32, i32,
+                                          ctypes.c_int, f32, vp, vp, vp, sz, vp]
+        lib.star_phase2_query.restype = ctypes.c_int
         lib.star_decode_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
         lib.star_decode_workspace_bytes.restype = sz
         lib.star_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32, i32,
@@ -227,6 +232,37 @@ def decode_workspace(L: int, tail_cap: int, n_shards: int, hq: int, hkv: int, d:
     return torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
 
 
+def star_phase2_query_workspace_bytes(rows: int, n_shards: int, hq: int, hkv: int, d: int) -> int:
+    return int(load_library().star_phase2_query_workspace_bytes(rows, n_shards, hq, hkv, d))
+
+
+def star_phase2_query(q, k_ctx, v_ctx, bounds, k_tail, v_tail, tail_len: int, o=None, lse=None,
+                      workspace=None, scale=None, want_lse: bool = True, stream=None):
+    """Query encoding on the query host: q [Hq,rows,d] are the last `rows` of the tail's
+    tail_len valid tokens; caches [Hkv,L,d] and [Hkv,tail_cap,d]; bounds: S+1 host ints."""
+    torch = _torch()
+    hq, rows, d = q.shape
+    hkv, L, _ = k_ctx.shape
+    tail_cap = k_tail.shape[1]
+    n_shards = len(bounds) - 1
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((hq, rows), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = star_phase2_query_workspace_bytes(rows, n_shards, hq, hkv, d)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    b = (ctypes.c_int64 * (n_shards + 1))(*[int(x) for x in bounds])
+    st = load_library().star_phase2_query(
+        _dev(q, "q"), rows, _same(k_ctx, q, "k_ctx", (hkv, L, d)), _same(v_ctx, q, "v_ctx", (hkv, L, d)), L, b,
+        n_shards, _same(k_tail, q, "k_tail", (hkv, tail_cap, d)), _same(v_tail, q, "v_tail", (hkv, tail_cap, d)),
+        tail_len, tail_cap, hq, hkv, d, _dt(q), _scale(d, scale), _same(o, q, "o", (hq, rows, d)),
+        ctypes.c_void_p(0) if lse is None else _f32(lse, "lse", (hq, rows)),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "star_phase2_query")
+    return o, lse
+
+
 def star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, tail_len: int,
                      o=None, lse=None, workspace=None, scale=None, want_lse: bool = True, stream=None):
     """One generated token: q_new [Hq,d], k_new/v_new [Hkv,d]; caches [Hkv,L,d] and
@@ -257,5 +293,6 @@ def star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, 
 __all__ = [
     "CONFIGS", "StarConfig", "n_blocks", "shard_bounds", "load_library", "StarError",
     "star_phase1_encode", "star_phase2_workspace_bytes", "star_phase2_partial", "star_softmax_merge",
+    "star_phase2_query_workspace_bytes", "star_phase2_query",
     "star_decode_workspace_bytes", "star_decode_step", "decode_workspace", "STAR_F32", "STAR_BF16",
 ]

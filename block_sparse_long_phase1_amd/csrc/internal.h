@@ -6,6 +6,22 @@
 
 namespace star {
 
+// Key partitions of one Phase-2 partial launch.  Partition i holds keys [0, n_kv[i]) at
+// k[i] / v[i], kv heads head_stride[i] elements apart; query row r sees token t iff
+// causal[i] < 0 or t <= causal[i] + r.  Partitions are cut into splits of split_len keys;
+// partition i owns global splits [split_prefix[i], split_prefix[i + 1]).
+constexpr int kMaxParts = 65;
+struct PartPlan {
+    int n_parts;
+    int64_t split_len;
+    const uint16_t* k[kMaxParts];
+    const uint16_t* v[kMaxParts];
+    int64_t head_stride[kMaxParts];
+    int64_t n_kv[kMaxParts];
+    int64_t causal[kMaxParts];
+    int32_t split_prefix[kMaxParts + 1];
+};
+
 // Arguments of the bf16 MFMA attention kernel (Phase 1 and Phase-2 partials).
 struct AttnMfmaArgs {
     const uint16_t* q;
@@ -21,11 +37,12 @@ struct AttnMfmaArgs {
     uint16_t* o;
     float* lse;
     // Phase-2 partial
-    int64_t rows, n_kv, causal_offset, split_len;
+    int64_t rows;
     int64_t n_row_tiles;
-    float* a_out;
+    float* a_out;     // [splits][hq][rows][d], m and l [splits][hq][rows]
     float* m_out;
     float* l_out;
+    PartPlan plan;
 };
 
 bool attn_mfma_supported(int d, int hq, int hkv);
@@ -36,13 +53,17 @@ hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16
                               uint16_t* o, float* lse, int64_t L, int64_t block, int64_t anchor,
                               int hq, int hkv, float scale, hipStream_t stream);
 
-void partial_mfma_plan(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv,
-                       int* n_row_tiles, int* n_splits, int64_t* split_len);
+// Cut the partitions of `plan` (n_parts, n_kv set) into key splits: fills split_len and
+// split_prefix and returns the number of query-row tiles.  Splits aim at one workgroup
+// per compute unit with at least 8 key tiles each.
+int partial_mfma_plan(PartPlan& plan, int32_t rows, int32_t hq, int32_t hkv);
+// Upper bound on the splits partial_mfma_plan makes for n_parts partitions.
+int64_t partial_mfma_max_splits(int32_t rows, int32_t hq, int32_t hkv, int n_parts);
 
-hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, const uint16_t* k, const uint16_t* v,
-                               int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
-                               int hq, int hkv, float scale, float* a_out, float* m_out, float* l_out,
-                               int n_splits, int64_t split_len, int n_row_tiles, hipStream_t stream);
+// Partials of every split of `plan` into a_out / m_out / l_out (global split order).
+hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, float scale,
+                               const PartPlan& plan, int n_row_tiles, float* a_out, float* m_out,
+                               float* l_out, hipStream_t stream);
 
 // Log-space merge of n_parts partials laid out [n_parts][n_rows][d] / [n_parts][n_rows].
 // Writes o ([n_rows][d], fp32 or bf16 per out_bf16), and optionally lse, or (m, l).

@@ -120,6 +120,9 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     int64_t row0, row_end;        // query rows [row0, row_end) valid for this workgroup
     KeyPlan kp;
     int split = 0;
+    const uint16_t* kptr = p.k;   // this work item's key partition
+    const uint16_t* vptr = p.v;
+    int64_t hstride = p.kv_head_stride;
     if (MODE == 0) {
         // Heaviest tiles first: last row tiles of blocks >= 1, then block 0.
         int64_t blk, rt;
@@ -149,22 +152,30 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         kp.diag = 0;
         kp.kmax = p.L;
     } else {
+        // Split `split` of partition `part` (global split order), row tile rt.
+        const PartPlan& pl = p.plan;
         const int64_t rt = rank % p.n_row_tiles;
         split = (int)(rank / p.n_row_tiles);
+        int part = 0;
+        while (split >= pl.split_prefix[part + 1]) ++part;
         row0 = rt * p.rows_per_wg;
         row_end = row0 + p.rows_per_wg < p.rows ? row0 + p.rows_per_wg : p.rows;
-        const int64_t lo = (int64_t)split * p.split_len;
-        int64_t hi = lo + p.split_len < p.n_kv ? lo + p.split_len : p.n_kv;
-        kp.causal = p.causal_offset >= 0;
-        kp.diag = p.causal_offset;
+        const int64_t n_kv = pl.n_kv[part];
+        const int64_t lo = (int64_t)(split - pl.split_prefix[part]) * pl.split_len;
+        int64_t hi = lo + pl.split_len < n_kv ? lo + pl.split_len : n_kv;
+        kp.causal = pl.causal[part] >= 0;
+        kp.diag = pl.causal[part];
         if (kp.causal) {
-            const int64_t lim = p.causal_offset + row_end;  // keys >= lim are invisible to every row here
+            const int64_t lim = kp.diag + row_end;  // keys >= lim are invisible to every row here
             hi = hi < lim ? hi : lim;
         }
         kp.a_lo = kp.a_hi = 0;
         kp.b_lo = lo;
         kp.b_hi = hi > lo ? hi : lo;
-        kp.kmax = p.n_kv;
+        kp.kmax = n_kv;
+        kptr = pl.k[part];
+        vptr = pl.v[part];
+        hstride = pl.head_stride[part];
     }
     kp.nta = (int)((kp.a_hi - kp.a_lo + kBN - 1) / kBN);
     kp.ntb = (int)((kp.b_hi - kp.b_lo + kBN - 1) / kBN);
@@ -197,8 +208,8 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     float lsum = 0.f;      // this lane's half of the row sum
     const float sl2 = p.scale_log2;
 
-    const uint16_t* kbase = p.k + (int64_t)g * p.kv_head_stride;
-    const uint16_t* vbase = p.v + (int64_t)g * p.kv_head_stride;
+    const uint16_t* kbase = kptr + (int64_t)g * hstride;
+    const uint16_t* vbase = vptr + (int64_t)g * hstride;
     const int kmax = (int)kp.kmax;
     const int a_lo = (int)kp.a_lo, b_lo = (int)kp.b_lo;
     auto tile_key0 = [&](int j) -> int { return j < kp.nta ? a_lo + j * kBN : b_lo + (j - kp.nta) * kBN; };
@@ -414,44 +425,53 @@ hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16
     return hipGetLastError();
 }
 
-void partial_mfma_plan(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv,
-                       int* n_row_tiles, int* n_splits, int64_t* split_len) {
+static int partial_splits_wanted(int32_t rows, int32_t hq, int32_t hkv, int* n_row_tiles) {
     const int G = hq / hkv;
     const int rw = kQPB / G;
     const int nrt = (rows + rw - 1) / rw;
-    const int64_t tiles = (n_kv + kBN - 1) / kBN;
     const int64_t base = (int64_t)hkv * nrt;
-    // Aim for at least two workgroups per compute unit (256 CUs).
-    int64_t want = (512 + base - 1) / base;
-    if (want > tiles) want = tiles;
-    if (want < 1) want = 1;
-    int64_t tiles_per_split = (tiles + want - 1) / want;
-    if (tiles_per_split < 1) tiles_per_split = 1;
-    int64_t ns = (tiles + tiles_per_split - 1) / tiles_per_split;
-    if (ns < 1) ns = 1;
     *n_row_tiles = nrt;
-    *n_splits = (int)ns;
-    *split_len = tiles_per_split * kBN;
+    // One workgroup of eight waves fills a compute unit; aim for one per CU (256).
+    return (int)(base >= 256 ? 1 : 256 / base);
 }
 
-hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, const uint16_t* k, const uint16_t* v,
-                               int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
-                               int hq, int hkv, float scale, float* a_out, float* m_out, float* l_out,
-                               int n_splits, int64_t split_len, int n_row_tiles, hipStream_t stream) {
+int partial_mfma_plan(PartPlan& plan, int32_t rows, int32_t hq, int32_t hkv) {
+    int nrt;
+    const int want = partial_splits_wanted(rows, hq, hkv, &nrt);
+    int64_t total_tiles = 0;
+    for (int i = 0; i < plan.n_parts; ++i) total_tiles += (plan.n_kv[i] + kBN - 1) / kBN;
+    int64_t tps = (total_tiles + want - 1) / want;
+    if (tps < 8) tps = 8;   // enough tiles per split to amortise the partial's write and merge
+    plan.split_len = tps * kBN;
+    plan.split_prefix[0] = 0;
+    for (int i = 0; i < plan.n_parts; ++i) {
+        int64_t ns = (plan.n_kv[i] + plan.split_len - 1) / plan.split_len;
+        if (ns < 1) ns = 1;   // an empty partition still reports its (empty) partial
+        plan.split_prefix[i + 1] = plan.split_prefix[i] + (int32_t)ns;
+    }
+    return nrt;
+}
+
+int64_t partial_mfma_max_splits(int32_t rows, int32_t hq, int32_t hkv, int n_parts) {
+    int nrt;
+    // ceil(tiles_i / tps) <= tiles_i / tps + 1 and sum(tiles_i) / tps <= want.
+    return (int64_t)partial_splits_wanted(rows, hq, hkv, &nrt) + n_parts;
+}
+
+hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, float scale,
+                               const PartPlan& plan, int n_row_tiles, float* a_out, float* m_out,
+                               float* l_out, hipStream_t stream) {
     AttnMfmaArgs a = {};
-    a.q = q; a.k = k; a.v = v;
+    a.q = q;
     a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
     a.rows_per_wg = kQPB / a.G;
     a.q_rows = rows;
     a.rows = rows;
-    a.kv_head_stride = kv_head_stride;
-    a.n_kv = n_kv;
-    a.causal_offset = causal_offset;
     a.scale_log2 = scale * kLog2e;
     a.a_out = a_out; a.m_out = m_out; a.l_out = l_out;
     a.n_row_tiles = n_row_tiles;
-    a.split_len = split_len;
-    const int64_t grid = (int64_t)hkv * n_row_tiles * n_splits;
+    a.plan = plan;
+    const int64_t grid = (int64_t)hkv * n_row_tiles * plan.split_prefix[plan.n_parts];
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();

@@ -125,9 +125,11 @@ star_status_t star_phase1_encode(const void* q, const void* k, const void* v, vo
 size_t star_phase2_workspace_bytes(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv, int32_t d) {
     if (rows < 1 || n_kv < 0 || hq < 1 || hkv < 1 || hq % hkv || d < 1) return 0;
     if (!star::attn_mfma_supported(d, hq, hkv)) return 0;
-    int nrt, ns;
-    int64_t split_len;
-    star::partial_mfma_plan(rows, n_kv, hq, hkv, &nrt, &ns, &split_len);
+    star::PartPlan plan = {};
+    plan.n_parts = 1;
+    plan.n_kv[0] = n_kv;
+    star::partial_mfma_plan(plan, rows, hq, hkv);
+    const int32_t ns = plan.split_prefix[1];
     return ns > 1 ? partials_bytes(ns, (int64_t)hq * rows, d) : 0;
 }
 
@@ -156,13 +158,18 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
             if (n_kv > star::attn_mfma_max_tokens())
                 return fail(STAR_ERR_UNSUPPORTED, "n_kv (%lld) above %lld tokens per partition", (long long)n_kv,
                             (long long)star::attn_mfma_max_tokens());
-            int nrt, ns;
-            int64_t split_len;
-            star::partial_mfma_plan(rows, n_kv, hq, hkv, &nrt, &ns, &split_len);
+            star::PartPlan plan = {};
+            plan.n_parts = 1;
+            plan.k[0] = static_cast<const uint16_t*>(k);
+            plan.v[0] = static_cast<const uint16_t*>(v);
+            plan.head_stride[0] = kv_head_stride;
+            plan.n_kv[0] = n_kv;
+            plan.causal[0] = causal_offset < 0 ? -1 : causal_offset;
+            const int nrt = star::partial_mfma_plan(plan, rows, hq, hkv);
+            const int32_t ns = plan.split_prefix[1];
             if (ns == 1) {
-                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, static_cast<const uint16_t*>(k),
-                                              static_cast<const uint16_t*>(v), kv_head_stride, n_kv, causal_offset,
-                                              hq, hkv, scale, a_out, m_out, l_out, 1, split_len, nrt, stream);
+                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, scale, plan, nrt,
+                                              a_out, m_out, l_out, stream);
                 if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
             } else {
                 size_t need = partials_bytes(ns, (int64_t)hq * rows, d);
@@ -171,9 +178,8 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
                                 need, workspace ? workspace_bytes : (size_t)0);
                 float *wa, *wm, *wl;
                 partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
-                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, static_cast<const uint16_t*>(k),
-                                              static_cast<const uint16_t*>(v), kv_head_stride, n_kv, causal_offset,
-                                              hq, hkv, scale, wa, wm, wl, ns, split_len, nrt, stream);
+                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, scale, plan, nrt,
+                                              wa, wm, wl, stream);
                 if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
                 e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, a_out, false, nullptr, m_out, l_out, stream);
                 if (e != hipSuccess) return hip_fail(e, "star_phase2_partial merge launch");
@@ -192,6 +198,90 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
         return ok();
     } catch (...) {
         return fail(STAR_ERR_HIP, "star_phase2_partial: internal error");
+    }
+}
+
+// ------------------------------------------------------------------------ Phase 2 query
+size_t star_phase2_query_workspace_bytes(int32_t rows, int32_t n_shards, int32_t hq, int32_t hkv, int32_t d) {
+    if (rows < 1 || n_shards < 1 || n_shards > 64 || hq < 1 || hkv < 1 || hq % hkv || d < 1) return 0;
+    if (!star::attn_mfma_supported(d, hq, hkv)) return 0;
+    return partials_bytes(star::partial_mfma_max_splits(rows, hq, hkv, n_shards + 1), (int64_t)hq * rows, d);
+}
+
+star_status_t star_phase2_query(const void* q, int32_t rows, const void* k_ctx, const void* v_ctx, int64_t L,
+                                const int64_t* shard_bounds, int32_t n_shards, const void* k_tail,
+                                const void* v_tail, int64_t tail_len, int64_t tail_cap, int32_t hq, int32_t hkv,
+                                int32_t d, star_dtype_t dt, float scale, void* o, float* lse, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    try {
+        if (!q || !k_ctx || !v_ctx || !k_tail || !v_tail || !o || !shard_bounds)
+            return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+        if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
+        if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
+        if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
+        if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
+            return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
+        for (int r = 0; r < n_shards; ++r)
+            if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
+        if (tail_len < rows || tail_len > tail_cap)
+            return fail(STAR_ERR_INVALID_ARG, "need rows <= tail_len <= tail_cap (rows %d, tail_len %lld, tail_cap %lld)",
+                        rows, (long long)tail_len, (long long)tail_cap);
+        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        star_status_t s = check_heads(hq, hkv, d, dt);
+        if (s != STAR_OK) return s;
+        if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(v_ctx) || !aligned16(k_tail) || !aligned16(v_tail) ||
+            !aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+            return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+        const int64_t causal = tail_len - rows;   // row i sees query-host tokens t <= causal + i
+        hipError_t e;
+        if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
+            if (L > star::attn_mfma_max_tokens() || tail_cap > star::attn_mfma_max_tokens())
+                return fail(STAR_ERR_UNSUPPORTED, "more than %lld tokens per kv head", (long long)star::attn_mfma_max_tokens());
+            star::PartPlan plan = {};
+            plan.n_parts = n_shards + 1;
+            for (int r = 0; r < n_shards; ++r) {
+                plan.k[r] = static_cast<const uint16_t*>(k_ctx) + shard_bounds[r] * d;
+                plan.v[r] = static_cast<const uint16_t*>(v_ctx) + shard_bounds[r] * d;
+                plan.head_stride[r] = L * d;
+                plan.n_kv[r] = shard_bounds[r + 1] - shard_bounds[r];
+                plan.causal[r] = -1;
+            }
+            plan.k[n_shards] = static_cast<const uint16_t*>(k_tail);
+            plan.v[n_shards] = static_cast<const uint16_t*>(v_tail);
+            plan.head_stride[n_shards] = tail_cap * d;
+            plan.n_kv[n_shards] = tail_len;
+            plan.causal[n_shards] = causal;
+            const int nrt = star::partial_mfma_plan(plan, rows, hq, hkv);
+            const int32_t ns = plan.split_prefix[plan.n_parts];
+            const int64_t n_max = star::partial_mfma_max_splits(rows, hq, hkv, plan.n_parts);
+            if (ns > n_max) return fail(STAR_ERR_HIP, "star_phase2_query: split plan exceeds its bound");
+            const size_t need = partials_bytes(n_max, (int64_t)hq * rows, d);
+            if (!workspace || workspace_bytes < need || !aligned16(workspace))
+                return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                            workspace ? workspace_bytes : (size_t)0);
+            float *wa, *wm, *wl;
+            partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
+            e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, scale, plan, nrt,
+                                          wa, wm, wl, stream);
+            if (e != hipSuccess) return hip_fail(e, "star_phase2_query launch");
+            e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, o, true, lse, nullptr, nullptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "star_phase2_query merge launch");
+        } else {
+            star::RowAttnArgs a = {};
+            a.q = q; a.q_rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
+            a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 1;
+            a.n_seg = 2;
+            a.seg[0].k = k_ctx; a.seg[0].v = v_ctx; a.seg[0].head_stride = L * d;
+            a.seg[0].n = L; a.seg[0].causal_lim = -1;
+            a.seg[1].k = k_tail; a.seg[1].v = v_tail; a.seg[1].head_stride = tail_cap * d;
+            a.seg[1].n = tail_len; a.seg[1].causal_lim = causal;
+            a.o = o; a.lse = lse;
+            e = star::launch_row_attn(a, rows, stream);
+            if (e != hipSuccess) return hip_fail(e, "star_phase2_query launch");
+        }
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_phase2_query: internal error");
     }
 }
 

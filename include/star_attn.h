@@ -127,6 +127,43 @@ star_status_t star_phase2_partial(const void *q, int32_t rows,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Phase 2 query encoding on the query host, every partition in one call.
+ * [SUM] 3.4 Phase 2 Steps 1-5; [README] "Phase 2 - Query Processing and Token
+ * Generation".
+ *
+ * The `rows` query tokens are the last `rows` entries of the query host's cache
+ * (their k/v already stored there): query row i sits at cache position
+ * c_i = tail_len - rows + i and sees every context token plus cache positions
+ * [0, c_i].  The local partial of each context shard and of the query host's
+ * cache is computed and all are merged in log space, which gives the exact
+ * global attention of the query rows.
+ *
+ *   q [hq, rows, d] (dt); rows >= 1
+ *   k_ctx, v_ctx [hkv, L, d]                context cache (dt), L >= 1
+ *   shard_bounds (host) int64[n_shards + 1]: 0 = b_0 <= b_1 <= ... <= b_S = L;
+ *                                            1 <= n_shards <= 64
+ *   k_tail, v_tail [hkv, tail_cap, d]       query-host cache (dt); entries
+ *                                           [0, tail_len) are valid
+ *   rows <= tail_len <= tail_cap.
+ *   o [hq, rows, d] (dt), lse [hq, rows] fp32 or NULL
+ *   workspace: star_phase2_query_workspace_bytes(rows, n_shards, hq, hkv, d)
+ *         bytes (may be 0 for shapes without the MFMA path; then workspace may
+ *         be NULL).  Scratch only: its contents need no initialisation.
+ * bf16 with d = 128: two kernel launches (the partials of every key split of
+ * every partition, then their merge).  Other shapes: one vector-path launch.
+ */
+size_t star_phase2_query_workspace_bytes(int32_t rows, int32_t n_shards, int32_t hq, int32_t hkv, int32_t d);
+
+star_status_t star_phase2_query(const void *q, int32_t rows,
+                                const void *k_ctx, const void *v_ctx, int64_t L,
+                                const int64_t *shard_bounds, int32_t n_shards,
+                                const void *k_tail, const void *v_tail, int64_t tail_len, int64_t tail_cap,
+                                int32_t hq, int32_t hkv, int32_t d,
+                                star_dtype_t dt, float scale,
+                                void *o, float *lse,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Global aggregation of partitions in log space.
  * [README] "Phase 2" (s_global = sum s_h, A_global = sum (s_h/s_global) A_h);
  * [SUM] 3.4 Phase 2 Step 5 (the same sum kept in log space).

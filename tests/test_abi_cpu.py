@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -94,7 +94,28 @@ def test_decode_validation(lib):
     assert d(*args(good, 2, 0, 8, 16)) == 4                        # workspace too small
 
 
+def test_query_validation(lib):
+    q = lib.star_phase2_query
+    B = ctypes.c_int64 * 3
+    good = B(0, 50, 100)
+    args = lambda rows, bounds, n_sh, tl, tc, ws: (FAKE, rows, FAKE, FAKE, 100, bounds, n_sh, FAKE, FAKE, tl, tc,
+                                                  4, 2, 128, 1, 0.1, FAKE, NULL, FAKE, ws, NULL)
+    assert q(*args(8, B(0, 60, 50), 2, 8, 8, 1 << 30)) == 1          # not monotone
+    assert q(*args(8, B(0, 50, 99), 2, 8, 8, 1 << 30)) == 1          # does not end at L
+    assert q(*args(0, good, 2, 8, 8, 1 << 30)) == 1                  # no rows
+    assert q(*args(8, good, 2, 7, 8, 1 << 30)) == 1                  # fewer cached tokens than rows
+    assert q(*args(8, good, 2, 9, 8, 1 << 30)) == 1                  # tail_len > tail_cap
+    assert q(*args(8, good, 65, 8, 8, 1 << 30)) == 1                 # too many shards
+    assert q(*args(8, good, 2, 8, 8, 16)) == 4                       # workspace too small
+    a = list(args(8, good, 2, 8, 8, 1 << 30))
+    a[0] = NULL
+    assert q(*a) == 1                                                # null q
+
+
 def test_workspace_queries(lib):
+    assert lib.star_phase2_query_workspace_bytes(128, 4, 32, 8, 128) > 0
+    assert lib.star_phase2_query_workspace_bytes(128, 0, 32, 8, 128) == 0
+    assert lib.star_phase2_query_workspace_bytes(16, 2, 1, 1, 64) == 0  # vector path needs none
     assert lib.star_decode_workspace_bytes(32768, 160, 4, 32, 8, 128) > 0
     assert lib.star_decode_workspace_bytes(0, 160, 4, 32, 8, 128) == 0
     assert lib.star_phase2_workspace_bytes(128, 0, 32, 8, 128) == 0

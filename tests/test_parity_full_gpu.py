@@ -2,8 +2,8 @@
 
 Phase 1 runs over the whole context; the oracle recomputes a seeded sample of rows (block
 edges, key-tile edges, the middle and random rows, all q heads each).  The query phase runs
-the same S+1 partial calls and merge as the benchmark; the oracle recomputes sampled query
-rows.  Every decode step runs; the oracle recomputes the first and the last.  Outputs must
+as the benchmark runs it (star_phase2_query, every partition in one call) and also as S+1
+separate partial calls plus a merge; the oracle recomputes sampled query rows of both.  Every decode step runs; the oracle recomputes the first and the last.  Outputs must
 also be finite everywhere.
 """
 import numpy as np
@@ -73,9 +73,10 @@ def test_full_workload(name):
     v_tail = torch.zeros_like(k_tail)
     k_tail[:, :cfg.lq] = x["k_qry"]
     v_tail[:, :cfg.lq] = x["v_qry"]
-    oq, lq_lse = _query_phase(cfg, x, bounds, k_tail, v_tail)
+    oq, lq_lse = sa.star_phase2_query(x["q_qry"], k, v, bounds, k_tail, v_tail, cfg.lq)
+    op, lp_lse = _query_phase(cfg, x, bounds, k_tail, v_tail)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(lq_lse).all())
+    assert bool(torch.isfinite(lq_lse).all()) and bool(torch.isfinite(lp_lse).all())
     kq, vq = x["k_qry"].cpu(), x["v_qry"].cpu()
     for i in sorted({0, 1, cfg.lq // 2, cfg.lq - 1}):
         qi = x["q_qry"][:, i:i + 1].cpu()
@@ -85,6 +86,8 @@ def test_full_workload(name):
                                   np.stack([p[2] for p in parts]))
         assert_out(oq[:, i:i + 1], ro_q, "%s query row %d O" % (name, i))
         assert_lse(lq_lse[:, i:i + 1], rl_q, "%s query row %d LSE" % (name, i))
+        assert_out(op[:, i:i + 1], ro_q, "%s query row %d O (per partition)" % (name, i))
+        assert_lse(lp_lse[:, i:i + 1], rl_q, "%s query row %d LSE (per partition)" % (name, i))
         if cfg.needle and i == 0:
             for g in range(cfg.hkv):
                 h = g * cfg.G

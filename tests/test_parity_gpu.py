@@ -200,11 +200,14 @@ def test_phase2_query_and_decode(hq, hkv, L, b, S, lq, T, dtype, d):
     k_tail[:, :lq] = x["k_qry"]
     v_tail[:, :lq] = x["v_qry"]
     o, lse = _run_query_phase(cfg, x, bounds, k_tail, v_tail)
+    of, lf = sa.star_phase2_query(x["q_qry"], k, v, bounds, k_tail, v_tail, lq)
     torch.cuda.synchronize()
     ro, rl = oracle.phase2_query(x["q_qry"].cpu(), k.cpu(), v.cpu(), bounds, x["k_qry"].cpu(), x["v_qry"].cpu())
     tol = dict(max_abs=2e-2, mean_abs=2e-3) if dtype == "bf16" else dict(max_abs=1e-5, mean_abs=1e-6)
     assert_out(o, ro, "query O", **tol)
     assert_lse(lse, rl, "query LSE", rel=1e-5 if dtype == "bf16" else 1e-6)
+    assert_out(of, ro, "fused query O", **tol)
+    assert_lse(lf, rl, "fused query LSE", rel=1e-5 if dtype == "bf16" else 1e-6)
     ws = sa.decode_workspace(L, cfg.tail_cap, S, hq, hkv, d, DEV)
     for t in range(T):
         od, ld = sa.star_decode_step(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k, v, bounds,
@@ -215,6 +218,34 @@ def test_phase2_query_and_decode(hq, hkv, L, b, S, lq, T, dtype, d):
                                         v_tail.cpu(), lq + t + 1)
         assert_out(od, rod, "decode O step %d" % t, **tol)
         assert_lse(ld, rld, "decode LSE step %d" % t, rel=1e-5 if dtype == "bf16" else 1e-6)
+
+
+@pytest.mark.parametrize("hq,hkv,L,bounds,rows,tail_len,tail_cap", [
+    (8, 2, 1000, [0, 250, 250, 900, 1000], 40, 40, 48),        # an empty shard, ragged shards
+    (16, 2, 2500, [0, 1300, 2500], 9, 30, 33),                 # G=8; query rows after 21 cached tokens
+    (4, 4, 700, [0, 700], 1, 1, 1),                            # G=1, one row, one cached token
+    (8, 1, 6000, [0, 1500, 3000, 4500, 6000], 300, 300, 310),  # several row tiles and key splits
+])
+def test_phase2_query_fused(hq, hkv, L, bounds, rows, tail_len, tail_cap):
+    """star_phase2_query (every partition in one call) against the oracle's partials + merge."""
+    flush_print("phase2 query", hq, hkv, L, bounds, rows, tail_len)
+    cfg = _cfg(hq, hkv, L, L, L, lq=tail_len, T=1, S=len(bounds) - 1, seed=37)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    qr = p2["q_qry"][:, tail_len - rows:].contiguous()
+    k_tail = torch.zeros((hkv, tail_cap, 128), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :tail_len] = p2["k_qry"]
+    v_tail[:, :tail_len] = p2["v_qry"]
+    o, lse = sa.star_phase2_query(qr, k, v, bounds, k_tail, v_tail, tail_len)
+    torch.cuda.synchronize()
+    qc, kc, vc = qr.cpu(), k.cpu(), v.cpu()
+    parts = [oracle.partial(qc, kc, vc, lo, hi) for lo, hi in zip(bounds[:-1], bounds[1:])]
+    parts.append(oracle.partial(qc, k_tail.cpu(), v_tail.cpu(), 0, tail_len, tail_len - rows))
+    ro, rl = oracle.merge(np.stack([x[0] for x in parts]), np.stack([x[1] for x in parts]),
+                          np.stack([x[2] for x in parts]))
+    assert_out(o, ro, "O")
+    assert_lse(lse, rl, "LSE")
 
 
 def test_decode_empty_shard_and_first_token():
