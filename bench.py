@@ -11,8 +11,8 @@ Prints ONE JSON line.  `value` is context tokens per second of the whole step
 (L / step time).  `roofline` describes the dominant kernel (the Phase-1 MFMA kernel):
 algorithmic flops per launch / its average launch time measured with HIP events on the
 launch stream, against the bf16 dense MFMA peak.  `decode` reports the decode step's
-K/V stream rate (warm: inside the step; cold: after overwriting 1 GiB so the 256 MB
-last-level cache holds no K/V).  `cpu_baseline` times the fp64 oracle on a bounded sample
+K/V stream rate (warm: inside the step; cold: after overwriting 1 GiB and reading it back,
+so the 256 MB last-level cache holds no K/V and no dirty lines).  `cpu_baseline` times the fp64 oracle on a bounded sample
 of Phase-1 rows on the host's cores.
 """
 from __future__ import annotations
@@ -181,11 +181,17 @@ def main():
         q_ms.append(e1.elapsed_time(e2))
         dec_ms.append(e3.elapsed_time(e4))
 
-    # ---- cold-cache decode: overwrite 1 GiB before each timed step (untimed)
+    # ---- cold-cache decode: overwrite 1 GiB, then read it back, before each timed step
+    # (untimed).  The read-back leaves the last-level cache holding clean lines of the
+    # flush buffer, so the timed step neither finds K/V cached nor pays for writing back
+    # the flush's dirty lines.  Nothing synchronises between these launches and the timed
+    # step, so the GPU is busy until the step starts and host launch time is not counted.
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     cold = []
     for r in range(args.cold_reps):
         flush.fill_(float(r))
+        torch.sum(flush, dim=0, out=sink)
         t = r % cfg.decode_steps
         a, b = ev(), ev()
         a.record(stream)
