@@ -15,11 +15,11 @@
 // cache (no one reads that slot from memory in the same launch).
 //
 // Each wave walks 32-key tiles of its chunk.  Both products run on
-// v_mfma_f32_32x32x16_bf16 with the G q heads as the 32-wide column block:
-// S^T = K Q^T takes K straight from 16-byte global loads, and O^T += V^T P^T
-// takes V^T from a wave-private LDS copy of the V tile (stored row-major,
-// read back with the transposing ds_read_b64_tr_b16).  Each wave keeps an
-// online softmax; the four waves are combined in LDS into one partial
+// v_mfma_f32_16x16x32_bf16 with the G <= 16 q heads as the 16-wide column
+// block: S^T = K Q^T takes K straight from 16-byte global loads, and
+// O^T += V^T P^T takes V^T from a wave-private LDS copy of the V tile (stored
+// row-major, read back with the transposing ds_read_b64_tr_b16).  Each wave
+// keeps an online softmax; the four waves are combined in LDS into one partial
 // (A, m, l) per chunk.  The last workgroup of a kv head to finish (an atomic
 // ticket in the workspace) merges that head's chunk partials in log space and
 // writes the output, then resets its ticket counter to zero.
@@ -65,10 +65,23 @@ __device__ __forceinline__ u32x2v lds_read_tr(const uint16_t* p) {
     lds_bf16x4* lp = (lds_bf16x4*)((__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(p)));
     return __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
+// Max / sum over lanes l, l^16, l^32, l^48 (one q column of the 16x16 layout).  With the
+// same register as both operands each swap returns {own, partner} in a lane-dependent order,
+// so only symmetric combinations are formed.
+__device__ __forceinline__ float quad_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return half_pair_max(x);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    return half_pair_sum(x);
+}
 }  // namespace
 
 template <int G>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 3)
 decode_kernel(const DecodeArgs p) {
     __shared__ __attribute__((aligned(16))) uint16_t vlds[kWaves][kT * kVPitch];
     __shared__ float wm[kWaves][G], wl[kWaves][G];
@@ -76,7 +89,7 @@ decode_kernel(const DecodeArgs p) {
     __shared__ unsigned ticket_sh;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int half = lane >> 5, col = lane & 31;
+    const int grp = lane >> 4, col = lane & 15;   // 16x16 MFMA layout: row group and column
     const int g = blockIdx.x % p.hkv;
     const int c = blockIdx.x / p.hkv;
     const DecodeChunkPlan& pl = p.plan;
@@ -113,37 +126,41 @@ decode_kernel(const DecodeArgs p) {
     const uint16_t* knew = p.k_new + (int64_t)g * kD;
     const uint16_t* vnew = p.v_new + (int64_t)g * kD;
 
-    // ---- Q^T as the B operand: column col = q head g*G + col (zero past G)
-    bf16x8 qb[8];
+    // ---- Q^T as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (grp, col)
+    //      holds q head g*G + col (zero past G), head-dim 32*dd + 8*grp .. +7.
+    bf16x8 qb[4];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+    for (int dd = 0; dd < 4; ++dd) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (col < G) w = *reinterpret_cast<const u32x4*>(p.q_new + (int64_t)(g * G + col) * kD + st * 16 + half * 8);
-        qb[st] = __builtin_bit_cast(bf16x8, w);
+        if (col < G) w = *reinterpret_cast<const u32x4*>(p.q_new + (int64_t)(g * G + col) * kD + dd * 32 + grp * 8);
+        qb[dd] = __builtin_bit_cast(bf16x8, w);
     }
 
-    f32x16 acc[4];
+    // O^T accumulators: head-dim block db of 16 rows; lane (grp, col) holds rows 16db + 4grp + r.
+    f32x4 acc[8];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float mref = kNoMax, lsum = 0.f;
     const float sl2 = p.sl2;
     uint16_t* vt = vlds[wave];
-    // transposing-read addressing inside a 16-key step (see the P.V comment below)
-    const int trow = 4 * half + ((lane & 15) >> 2);
-    const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+    // transposing-read addressing (see the P.V comment below)
+    const int trow = 4 * grp + (col >> 2);
+    const int tcol = 4 * (col & 3);
 
     const int n_tiles = (int)((hi - lo + kT - 1) / kT);
-    // K rows as the A operand (row = key k0 + col) and V row-major pieces for LDS, for the
-    // tile that starts at key k0.  Keys past the chunk are clamped to its last key.
+    // K operands (16-key block kb, head-dim block dd: key k0 + 16kb + col, head-dim 32dd + 8grp)
+    // and V row-major pieces for LDS, for the tile that starts at key k0.  Keys past the chunk
+    // are clamped to its last key.
     u32x4 ka[8], vr[8];
     auto load_tile = [&](int64_t k0) {
-        int64_t key = k0 + col;
-        key = key < hi ? key : hi - 1;
-        const uint16_t* src = key == new_key ? knew : kb + key * kD;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) ka[st] = *reinterpret_cast<const u32x4*>(src + st * 16 + half * 8);
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            int64_t key = k0 + 16 * kb2 + col;
+            key = key < hi ? key : hi - 1;
+            const uint16_t* src = key == new_key ? knew : kb + key * kD;
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) ka[kb2 * 4 + dd] = *reinterpret_cast<const u32x4*>(src + dd * 32 + grp * 8);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int cc = lane + 64 * i;
@@ -156,13 +173,17 @@ decode_kernel(const DecodeArgs p) {
     if (wave < n_tiles) load_tile(lo + (int64_t)wave * kT);
     for (int t = wave; t < n_tiles; t += kWaves) {
         const int64_t k0 = lo + (int64_t)t * kT;
-        // S^T = K Q^T, and this tile's V into the wave's LDS tile
-        f32x16 s;
+        // S^T = K Q^T: s[kb][r] is key k0 + 16kb + 4grp + r for q column col; and this tile's V
+        // into the wave's LDS tile
+        f32x4 s[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            s[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s, 0, 0, 0);
+            for (int dd = 0; dd < 4; ++dd)
+                s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kb2 * 4 + dd]), qb[dd],
+                                                                s[kb2], 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int cc = lane + 64 * i;
@@ -173,83 +194,75 @@ decode_kernel(const DecodeArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         if (t + kWaves < n_tiles) load_tile(k0 + (int64_t)kWaves * kT);
         __builtin_amdgcn_sched_barrier(0);
-        // mask keys past the chunk (score rows: key k0 + 8*(r/4) + 4*half + r%4)
         if (k0 + kT > hi) {
             const int lim = (int)(hi - k0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if ((r >> 2) * 8 + half * 4 + (r & 3) >= lim) s[r] = -INFINITY;
-        }
-        // online softmax with a lazily moved reference
-        float mx = s[0];
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = half_pair_max(mx) * sl2;
+                for (int r = 0; r < 4; ++r)
+                    if (16 * kb2 + 4 * grp + r >= lim) s[kb2][r] = -INFINITY;
+        }
+        // online softmax with a lazily moved reference; a column's 32 keys sit in lanes
+        // col, col+16, col+32, col+48
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = quad_max(mx) * sl2;
         if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleThreshold)) {
             const float nref = fmaxf(mref, mx);
             const float alpha = fast_exp2(mref - nref);
             mref = nref;
             lsum *= alpha;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            for (int db = 0; db < 8; ++db) acc[db] *= alpha;
         }
-        bf16x8 pb[2];
+        bf16x8 pb;
         {
             const float negm = -mref;
-            float ls = 0.f;
+            float e[8];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float e[8];
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    e[i] = fast_exp2(fmaf(s[8 * u + i], sl2, negm));
-                    ls += e[i];
-                }
-                u32x4 w;
-                w[0] = pack_bf16x2(e[0], e[1]);
-                w[1] = pack_bf16x2(e[2], e[3]);
-                w[2] = pack_bf16x2(e[4], e[5]);
-                w[3] = pack_bf16x2(e[6], e[7]);
-                pb[u] = __builtin_bit_cast(bf16x8, w);
-            }
-            lsum += ls;
+                for (int r = 0; r < 4; ++r) e[4 * kb2 + r] = fast_exp2(fmaf(s[kb2][r], sl2, negm));
+            lsum += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            u32x4 w;
+            w[0] = pack_bf16x2(e[0], e[1]);
+            w[1] = pack_bf16x2(e[2], e[3]);
+            w[2] = pack_bf16x2(e[4], e[5]);
+            w[3] = pack_bf16x2(e[6], e[7]);
+            pb = __builtin_bit_cast(bf16x8, w);
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // O^T += V^T P^T.  16-key step u: slot i of lane half h is key 16u + 8*(i/4) + 4h + i%4,
-        // the S^T accumulator layout.  In each 16-lane group of a transposing read, source lane
-        // s points at key (s/4) of its four-key set, columns 4*(s%4) .. +3 of the group's
-        // 16-wide head-dim slice; result lane i then holds column (i) of that slice for the
-        // four keys.  Two reads give the 8 slots: keys 16u + 4h + {0..3} and 16u + 8 + 4h + {0..3}.
+        // O^T += V^T P^T over the 32 keys.  k-slot i of lane group grp is key 4grp + i (i < 4)
+        // or 16 + 4grp + i - 4, the S^T layout above.  In each 16-lane group of a transposing
+        // read, source lane s points at key (s/4) of its four-key set and at columns
+        // 4*(s%4) .. +3 of the 16-wide head-dim block; result lane i then holds column i of
+        // the block for the four keys.  Two reads give the 8 slots.
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint16_t* base = vt + (16 * u + trow) * kVPitch + db * 32 + tcol;
-                const u32x2v a0 = lds_read_tr(base);
-                const u32x2v a1 = lds_read_tr(base + 8 * kVPitch);
-                const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[u], acc[db], 0, 0, 0);
-            }
+        for (int db = 0; db < 8; ++db) {
+            const uint16_t* base = vt + trow * kVPitch + db * 16 + tcol;
+            const u32x2v a0 = lds_read_tr(base);
+            const u32x2v a1 = lds_read_tr(base + 16 * kVPitch);
+            const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, acc[db], 0, 0, 0);
+        }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     // ---- combine the four waves into this chunk's partial
-    const float lw = half_pair_sum(lsum);
+    const float lw = quad_sum(lsum);
     if (col < G) {
-        if (half == 0) {
+        if (grp == 0) {
             wm[wave][col] = mref;
             wl[wave][col] = lw;
         }
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) wo[wave][col][db * 32 + (r >> 2) * 8 + half * 4 + (r & 3)] = acc[db][r];
+            for (int r = 0; r < 4; ++r) wo[wave][col][db * 16 + 4 * grp + r] = acc[db][r];
     }
     __syncthreads();
     for (int idx = tid; idx < G * kD; idx += kThreads) {
@@ -294,7 +307,7 @@ decode_kernel(const DecodeArgs p) {
         f32x4 o4[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) o4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll 2
         for (int ci = cg; ci < nc; ci += 16) {
             const int64_t row = (int64_t)ci * p.hq + h;
             const float m = p.pm[row], l = p.pl[row];
@@ -346,11 +359,11 @@ bool decode_bf16_supported(int d, int hq, int hkv) {
 }
 
 int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv) {
-    // About two resident workgroups per compute unit (256 CUs), all in one round: each kv
-    // head gets up to 440/hkv - 1 context chunks, spread over its shards by length, plus
+    // About three resident workgroups per compute unit (256 CUs), all in one round: each kv
+    // head gets up to 690/hkv - 1 context chunks, spread over its shards by length, plus
     // its query-host chunk(s).  Chunks are a multiple of the 4 x 32 keys one pass covers.
     const int64_t L = shard_bounds[n_shards] - shard_bounds[0];
-    int64_t budget = 440 / hkv - 1;
+    int64_t budget = 690 / hkv - 1;
     if (budget < n_shards) budget = n_shards;
     int64_t ch = 128;
     for (int r = 0; r < n_shards; ++r) {
@@ -367,7 +380,7 @@ int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv)
 int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv) {
     // The plan above gives each shard at most budget*len/L chunks (at least 1), hence at
     // most budget + n_shards context chunks, and the query host at most ceil(tail_cap/128).
-    int64_t budget = 440 / hkv - 1;
+    int64_t budget = 690 / hkv - 1;
     if (budget < n_shards) budget = n_shards;
     return budget + n_shards + (tail_cap + 127) / 128;
 }
