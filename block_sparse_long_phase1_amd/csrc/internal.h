@@ -30,6 +30,7 @@ struct AttnMfmaArgs {
     int64_t kv_head_stride;   // elements between kv heads
     int64_t q_rows;           // rows per q head in q (and in the outputs)
     int hq, hkv, G, rows_per_wg;
+    int head_major;           // Phase 1: work items ordered head by head (else heads interleave)
     float scale_log2;         // scale * log2(e)
     // Phase 1
     int64_t L, block, anchor;

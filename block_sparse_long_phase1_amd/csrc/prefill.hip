@@ -115,8 +115,20 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     const int col = lane & 31;    // query column inside the wave's 32-query block
 
     // ---------------------------------------------------------------- work item
-    const int g = blockIdx.x % p.hkv;
-    const int64_t rank = blockIdx.x / p.hkv;
+    // Work order.  Heads interleave (blockIdx % Hkv) while the whole K/V cache fits the
+    // 256 MB last-level cache: with 8 kv heads that pins each head to one XCD and its L2.
+    // Larger caches go head by head, so the workgroups running together share one head's
+    // anchor tiles in the last-level cache.
+    int g;
+    int64_t rank;
+    if (MODE == 0 && p.head_major) {
+        const int64_t per_head = p.tiles_ge1 + p.nt0;
+        g = (int)(blockIdx.x / per_head);
+        rank = blockIdx.x % per_head;
+    } else {
+        g = blockIdx.x % p.hkv;
+        rank = blockIdx.x / p.hkv;
+    }
     int64_t row0, row_end;        // query rows [row0, row_end) valid for this workgroup
     KeyPlan kp;
     int split = 0;
@@ -420,6 +432,7 @@ hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16
     a.tiles_ge1 = tiles_ge1;
     const int64_t tiles = tiles_ge1 + a.nt0;
     const int64_t grid = tiles * hkv;
+    a.head_major = 2.0 * hkv * (double)L * kD * 2 > 256.0 * (1 << 20);
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_mfma_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
