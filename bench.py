@@ -91,8 +91,8 @@ def calibrate_copy():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the whole path on a single MI355X "
-              "(--gpus %d requested); see the sharding design in DESIGN.md" % args.gpus)
+        print("bench.py measures one GPU only: the whole path runs on a single MI355X and no "
+              "multi-GPU sharding is implemented (--gpus %d requested)" % args.gpus)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
