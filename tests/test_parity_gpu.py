@@ -76,6 +76,25 @@ def test_phase1_bf16_vector_path_d64():
     assert_lse(lse, rl, "LSE")
 
 
+def test_phase1_head_by_head_order_ragged():
+    """A K/V cache above 256 MB takes the head-by-head work order; ragged last block, anchor
+    not a multiple of the key tile, sampled rows against the oracle."""
+    hq, hkv, L, b, a = 16, 8, 70000, 20000, 19999
+    flush_print("phase1 head-by-head", hq, hkv, L, b, a)
+    assert 2 * hkv * L * 128 * 2 > 256 << 20
+    cfg = _cfg(hq, hkv, L, b, a, seed=41)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    o, lse = sa.star_phase1_encode(q, k, v, b, a)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 63, 64, a - 1, a, b - 1, b, b + 1, 2 * b - 1, 2 * b, 3 * b, 3 * b + 1,
+                            L - 2, L - 1} | set(int(x) for x in np.random.default_rng(41).integers(0, L, 24))),
+                    dtype=np.int64)
+    ridx = torch.from_numpy(rows).to(DEV)
+    ro, rl = oracle.phase1(q[:, ridx].cpu(), k.cpu(), v.cpu(), b, a, rows=rows, q_sampled=True)
+    assert_out(o[:, ridx], ro, "O")
+    assert_lse(lse[:, ridx], rl, "LSE")
+
+
 def test_phase1_locality_bitwise():
     """Keys outside a row's visible set cannot change its output, bit for bit."""
     cfg = _cfg(8, 2, 768, 256, 256)
