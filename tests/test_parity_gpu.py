@@ -300,3 +300,51 @@ def test_decode_shard_split_invariance():
     for o, lse in outs[1:]:
         assert (o - outs[0][0]).abs().max().item() <= 1e-2
         assert (lse - outs[0][1]).abs().max().item() <= 1e-5 * max(1.0, outs[0][1].abs().max().item())
+
+
+def test_decode_steps_replayed_from_a_hip_graph():
+    """T decode steps captured in one HIP graph (the library allocates nothing and records no
+    memsets) replay bit-identically to the eager calls, with eager work between replays."""
+    cfg = _cfg(8, 2, 3000, 1000, 1000, lq=16, T=4, S=3, seed=43)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    bounds = shard_bounds(cfg.L, cfg.block, cfg.shards)
+    T, lq = cfg.decode_steps, cfg.lq
+
+    def fresh_tail():
+        kt = torch.zeros((cfg.hkv, cfg.tail_cap, cfg.d), dtype=torch.bfloat16, device=DEV)
+        vt = torch.zeros_like(kt)
+        kt[:, :lq] = p2["k_qry"]
+        vt[:, :lq] = p2["v_qry"]
+        return kt, vt
+
+    kt, vt = fresh_tail()
+    ws = sa.decode_workspace(cfg.L, cfg.tail_cap, cfg.shards, cfg.hq, cfg.hkv, cfg.d, DEV)
+    eager = []
+    for t in range(T):
+        o, l = sa.star_decode_step(p2["q_dec"][t], p2["k_dec"][t], p2["v_dec"][t], k, v, bounds, kt, vt, lq + t,
+                                   workspace=ws)
+        eager.append((o.clone(), l.clone()))
+    kt2, vt2 = fresh_tail()
+    ws2 = sa.decode_workspace(cfg.L, cfg.tail_cap, cfg.shards, cfg.hq, cfg.hkv, cfg.d, DEV)
+    outs = [(torch.empty((cfg.hq, cfg.d), dtype=torch.bfloat16, device=DEV),
+             torch.empty((cfg.hq,), dtype=torch.float32, device=DEV)) for _ in range(T)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(T):
+            sa.star_decode_step(p2["q_dec"][t], p2["k_dec"][t], p2["v_dec"][t], k, v, bounds, kt2, vt2, lq + t,
+                                o=outs[t][0], lse=outs[t][1], workspace=ws2)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for t in range(T):
+            assert torch.equal(outs[t][0], eager[t][0]), "replay %d step %d: O differs" % (rep, t)
+            assert torch.equal(outs[t][1], eager[t][1]), "replay %d step %d: LSE differs" % (rep, t)
+        assert torch.equal(kt2, kt) and torch.equal(vt2, vt)
+        # unrelated eager work between replays
+        sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor)
+        for t in range(T):
+            outs[t][0].zero_()
+            outs[t][1].zero_()
+        torch.cuda.synchronize()
