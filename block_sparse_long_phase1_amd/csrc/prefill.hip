@@ -52,6 +52,7 @@ constexpr int kKTileBytes = 16 * kKBlock;
 constexpr int kVTileBytes = 16 * kVBlock;
 constexpr int kStageBytes = kKTileBytes + kVTileBytes;
 constexpr float kRescaleThreshold = 8.0f;     // log2 units
+constexpr float kSumBound = 1048576.0f;       // 2^20
 
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
@@ -264,23 +265,26 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         const char* vp = vs + trow * kVBlock + tcol * 2;
 
         // ---- S^T = K Q^T, one 32-key block at a time, all eight K operands read first
+        auto scores = [&]() {
 #pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
-            u32x4 ka[8];
+            for (int kb = 0; kb < kKB; ++kb) {
+                u32x4 ka[8];
 #pragma unroll
-            for (int st = 0; st < 8; ++st)
-                ka[st] = *reinterpret_cast<const u32x4*>(kp + kb * 512 + st * 32);
+                for (int st = 0; st < 8; ++st)
+                    ka[st] = *reinterpret_cast<const u32x4*>(kp + kb * 512 + st * 32);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-            for (int st = 0; st < 8; ++st)
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s[kb],
-                                                               0, 0, 0);
-        }
+                for (int st = 0; st < 8; ++st)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s[kb],
+                                                                   0, 0, 0);
+            }
+        };
+        scores();
         mask(j);
 
         // ---- tile max; move the reference (and rescale) only if it grew past 2^8
-        {
+        auto rescale_to_max = [&]() {
             float mx = s[0][0];
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb)
@@ -298,7 +302,37 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
             }
+        };
+        // Phase-2 partials report the true max, so they take the max of every tile; Phase 1
+        // takes it on its first tile only (see below).
+        if (MODE == 1 || j == 0) rescale_to_max();
+
+        // ---- P^T = exp2(S^T - ref) in place, row sums from the unrounded values
+        auto exps = [&]() -> float {
+            const float negm = -mref;
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] = fast_exp2(fmaf(s[kb][r], sl2, negm));
+                    ls += s[kb][r];
+                }
+            return ls;
+        };
+        float ls = exps();
+        // Phase 1 keeps the tile when every row's sum of probabilities is at most 2^20: no
+        // probability overflowed and the accumulators stay far from the fp32 range, so the
+        // reference need not move.  Else (scores far above the reference) the scores are
+        // recomputed from the K tile, the reference moves to their max and the probabilities
+        // are redone.  This replaces a max over every tile's scores.
+        if (MODE == 0 && __builtin_amdgcn_ballot_w64(!(ls <= kSumBound))) {
+            scores();
+            mask(j);
+            rescale_to_max();
+            ls = exps();
         }
+        lsum += ls;
 
         // ---- V^T operands by transposing reads of the row-major V tile.  16-key step u:
         //      slot i of lane half h is key 16u + 8*(i/4) + 4h + i%4, the S^T layout.  In a
@@ -315,19 +349,6 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
                 va[u][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
             }
 
-        // ---- P^T = exp2(S^T - ref) in place, row sums from the unrounded values
-        {
-            const float negm = -mref;
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[kb][r] = fast_exp2(fmaf(s[kb][r], sl2, negm));
-                    ls += s[kb][r];
-                }
-            lsum += ls;
-        }
 
         // ---- O^T += V^T P^T
 #pragma unroll

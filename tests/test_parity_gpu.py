@@ -95,6 +95,23 @@ def test_phase1_head_by_head_order_ragged():
     assert_lse(lse[:, ridx], rl, "LSE")
 
 
+def test_phase1_scores_jumping_past_the_reference():
+    """A key scaled 30x in the middle of blocks makes scores jump far above the running
+    reference, so Phase 1 must move its reference mid-row (the recompute path)."""
+    hq, hkv, L, b, a = 8, 2, 2000, 640, 640
+    cfg = _cfg(hq, hkv, L, b, a, seed=47)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    k = k.clone()
+    for p in (300, 900, 1500, 1900):
+        k[:, p] = (k[:, p].float() * 30).to(k.dtype)
+    o, lse = sa.star_phase1_encode(q, k, v, b, a)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase1(q.cpu(), k.cpu(), v.cpu(), b, a)
+    assert float(np.max(rl)) > 60.0
+    assert_out(o, ro, "O")
+    assert_lse(lse, rl, "LSE")
+
+
 def test_phase1_locality_bitwise():
     """Keys outside a row's visible set cannot change its output, bit for bit."""
     cfg = _cfg(8, 2, 768, 256, 256)
