@@ -359,11 +359,11 @@ bool decode_bf16_supported(int d, int hq, int hkv) {
 }
 
 int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv) {
-    // About three resident workgroups per compute unit (256 CUs), all in one round: each kv
-    // head gets up to 690/hkv - 1 context chunks, spread over its shards by length, plus
+    // About one context chunk per compute unit (256 CUs), all in one round: each kv head gets
+    // up to 272/hkv - 1 context chunks, spread over its shards by length, plus
     // its query-host chunk(s).  Chunks are a multiple of the 4 x 32 keys one pass covers.
     const int64_t L = shard_bounds[n_shards] - shard_bounds[0];
-    int64_t budget = 690 / hkv - 1;
+    int64_t budget = 272 / hkv - 1;
     if (budget < n_shards) budget = n_shards;
     int64_t ch = 128;
     for (int r = 0; r < n_shards; ++r) {
@@ -380,7 +380,7 @@ int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv)
 int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv) {
     // The plan above gives each shard at most budget*len/L chunks (at least 1), hence at
     // most budget + n_shards context chunks, and the query host at most ceil(tail_cap/128).
-    int64_t budget = 690 / hkv - 1;
+    int64_t budget = 272 / hkv - 1;
     if (budget < n_shards) budget = n_shards;
     return budget + n_shards + (tail_cap + 127) / 128;
 }
