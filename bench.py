@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="8b_32k")
+    ap.add_argument("--block", type=int, default=None, help="override the workload's block size")
+    ap.add_argument("--anchor", type=int, default=None, help="override the workload's anchor size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-reps", type=int, default=8)
@@ -105,6 +107,11 @@ def main():
     from block_sparse_long_phase1_amd.configs import CONFIGS
 
     cfg = CONFIGS[args.config]
+    if args.block is not None or args.anchor is not None:
+        import dataclasses
+        blk = args.block if args.block is not None else cfg.block
+        anc = args.anchor if args.anchor is not None else min(cfg.anchor, blk)
+        cfg = dataclasses.replace(cfg, name="%s_b%d_a%d" % (cfg.name, blk, anc), block=blk, anchor=anc)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     print("bench: config %s, generating inputs" % cfg.name, file=sys.stderr, flush=True)
