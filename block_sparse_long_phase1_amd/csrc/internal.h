@@ -46,13 +46,14 @@ struct AttnMfmaArgs {
     PartPlan plan;
 };
 
+// bf16 MFMA kernels: head dim 64 or 128, G = hq / hkv dividing 256.
 bool attn_mfma_supported(int d, int hq, int hkv);
 // Largest per-kv-head token count the MFMA kernel addresses with 32-bit offsets.
-int64_t attn_mfma_max_tokens();
+int64_t attn_mfma_max_tokens(int d);
 
 hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               uint16_t* o, float* lse, int64_t L, int64_t block, int64_t anchor,
-                              int hq, int hkv, float scale, hipStream_t stream);
+                              int hq, int hkv, int d, float scale, hipStream_t stream);
 
 // Cut the partitions of `plan` (n_parts, n_kv set) into key splits: fills split_len and
 // split_prefix and returns the number of query-row tiles.  Splits aim at one workgroup
@@ -62,7 +63,7 @@ int partial_mfma_plan(PartPlan& plan, int32_t rows, int32_t hq, int32_t hkv);
 int64_t partial_mfma_max_splits(int32_t rows, int32_t hq, int32_t hkv, int n_parts);
 
 // Partials of every split of `plan` into a_out / m_out / l_out (global split order).
-hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, float scale,
+hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, int d, float scale,
                                const PartPlan& plan, int n_row_tiles, float* a_out, float* m_out,
                                float* l_out, hipStream_t stream);
 

@@ -9,6 +9,8 @@
 //     Phase 2 Step 3): no mask for a context shard, a causal offset for the
 //     query host's own cache; key splits of one partition are merged later.
 //
+// Head dim 64 or 128 (template parameter D).
+//
 // Work unit: one workgroup = 256 queries that share one kv head (G q heads x
 // 256/G consecutive rows), so each K/V tile staged in LDS feeds the whole GQA
 // group.  8 waves (two per SIMD), 32 queries each; every value stays in VGPRs.
@@ -37,20 +39,32 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kBN = 64;          // keys per tile
-constexpr int kD = 128;          // head dim of this kernel
 constexpr int kQPB = 256;        // queries per workgroup
 constexpr int kKB = kBN / 32;    // 32-key MFMA blocks per tile
-// LDS tile layout.  A tile's 64 key rows (256 B each) sit in 16 blocks of four rows,
-// block b holding rows b, b+16, b+32, b+48; consecutive rows therefore fall in
-// consecutive blocks.  Blocks are padded so that each starts 16 B (K) or 64 B (V)
-// further around the 256-byte bank cycle than the previous one: the 16 rows read by
-// a K operand read, and the 4 rows x 4 chunks of a transposing V read, then touch
-// distinct banks, and every operand address is one per-lane base plus a constant.
+// LDS tile layout for head dim D (rows of 2D bytes).  A tile's 64 key rows sit in 1 KB
+// blocks of 1024/(2D) rows: with NB = 64 / (rows per block) blocks, block b holds rows
+// b, b + NB, b + 2NB, ...; consecutive rows therefore fall in consecutive blocks.  Blocks
+// are padded so that each starts 16 B (K) or 64 B (V) further around the 256-byte bank
+// cycle than the previous one: the 16 rows read by a K operand read, and the 4 rows x 4
+// chunks of a transposing V read, then touch distinct banks, and every operand address
+// is one per-lane base plus a constant.
 constexpr int kKBlock = 1024 + 16;            // bytes per K block
 constexpr int kVBlock = 1024 + 64;            // bytes per V block
-constexpr int kKTileBytes = 16 * kKBlock;
-constexpr int kVTileBytes = 16 * kVBlock;
-constexpr int kStageBytes = kKTileBytes + kVTileBytes;
+template <int D>
+struct Geo {
+    static_assert(D == 64 || D == 128, "head dim");
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
+    static constexpr int kRowsPerBlock = 1024 / kRowBytes;
+    static constexpr int kBlocks = kBN / kRowsPerBlock;
+    static constexpr int kKTileBytes = kBlocks * kKBlock;
+    static constexpr int kVTileBytes = kBlocks * kVBlock;
+    static constexpr int kStageBytes = kKTileBytes + kVTileBytes;
+    static constexpr int kST = D / 16;                      // k-steps of S^T = K Q^T
+    static constexpr int kDB = D / 32;                      // 32-row blocks of O^T
+    // byte offset, inside the V tile, of row r + 8 relative to row r (r % NB < 8)
+    static constexpr int kPlus8 = (8 % kBlocks) * kVBlock + (8 / kBlocks) * kRowBytes;
+};
 constexpr float kRescaleThreshold = 8.0f;     // log2 units
 constexpr float kSumBound = 1048576.0f;       // 2^20
 
@@ -68,23 +82,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy one K/V tile straight from global memory into an LDS stage (no registers).
 // One instruction fills one 1 KB block (lane i writes bytes 16i .. 16i+15 of it):
-// row b + 16*(i/16), 16-byte chunk i%16.  Waves 0-3 fill the K blocks, waves 4-7 the
-// V blocks, four each.  Keys at or past `kmax` are clamped to kmax-1 (always a valid
-// row); their scores are masked later.  Key offsets from the kv head's base fit in
-// 32 bits (checked on the host).  `wave` must be wave-uniform.
+// row b + NB*(i / chunks per row), 16-byte chunk i % chunks per row.  Waves 0-3 fill
+// the K blocks, waves 4-7 the V blocks.  Keys at or past `kmax` are clamped to kmax-1
+// (always a valid row); their scores are masked later.  Key offsets from the kv head's
+// base fit in 32 bits (checked on the host).  `wave` must be wave-uniform.
+template <int D>
 __device__ __forceinline__ void dma_tile(char* stage, const uint16_t* __restrict__ kb,
                                          const uint16_t* __restrict__ vb, int key0, int kmax, int wave, int lane) {
+    using T = Geo<D>;
     const bool is_k = wave < 4;
     const char* src = reinterpret_cast<const char*>(is_k ? kb : vb);
-    char* dst = stage + (is_k ? 0 : kKTileBytes);
+    char* dst = stage + (is_k ? 0 : T::kKTileBytes);
     const int blk_bytes = is_k ? kKBlock : kVBlock;
     const int w4 = wave & 3;
+    constexpr int kPerWave = T::kBlocks / 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = w4 * 4 + i;
-        const int row = b + 16 * (lane >> 4);
+    for (int i = 0; i < kPerWave; ++i) {
+        const int b = w4 * kPerWave + i;
+        const int row = b + T::kBlocks * (lane / T::kChunks);
         const int key = min(key0 + row, kmax - 1);
-        const uint32_t off = (uint32_t)key * (kD * 2) + (uint32_t)(lane & 15) * 16u;
+        const uint32_t off = (uint32_t)key * T::kRowBytes + (uint32_t)(lane % T::kChunks) * 16u;
         __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_void*)(dst + b * blk_bytes), 16, 0, 0);
     }
 }
@@ -102,12 +119,14 @@ struct KeyPlan {
 
 }  // namespace
 
-// MODE 0 = Phase 1 encode, 1 = Phase 2 partial.
-template <int MODE>
+// MODE 0 = Phase 1 encode, 1 = Phase 2 partial; D = head dim (64 or 128).
+template <int MODE, int D>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_mfma_kernel(const AttnMfmaArgs p) {
-    __shared__ __attribute__((aligned(16))) char smem0[kStageBytes];
-    __shared__ __attribute__((aligned(16))) char smem1[kStageBytes];
+    using T = Geo<D>;
+    constexpr int kD = D;
+    __shared__ __attribute__((aligned(16))) char smem0[T::kStageBytes];
+    __shared__ __attribute__((aligned(16))) char smem1[T::kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -200,20 +219,20 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     const int qhead = g * p.G + qi / p.rows_per_wg;
     const int64_t qrow = row0 + qi % p.rows_per_wg;
     const bool qvalid = (qi / p.rows_per_wg) < p.G && qrow < row_end;
-    bf16x8 qb[8];
+    bf16x8 qb[T::kST];
     {
         const uint16_t* qp = p.q + ((int64_t)qhead * p.q_rows + (qvalid ? qrow : 0)) * kD;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
+        for (int st = 0; st < T::kST; ++st) {
             u32x4 w = {0u, 0u, 0u, 0u};
             if (qvalid) w = *reinterpret_cast<const u32x4*>(qp + st * 16 + half * 8);
             qb[st] = __builtin_bit_cast(bf16x8, w);
         }
     }
 
-    f32x16 acc[4];
+    f32x16 acc[T::kDB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
     float mref = kNoMax;   // reference max (log2 units) used in the exponent
@@ -256,26 +275,26 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
 
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     auto step = [&](int j, const char* cur, char* nxt) {
-        if (j + 1 < nt) dma_tile(nxt, kbase, vbase, tile_key0(j + 1), kmax, uwave, lane);
-        const char* vs = cur + kKTileBytes;
-        // K operand: row kb*32 + col, chunk 2*st + half.  Rows col and col+16 differ by 256 B
-        // inside a block; kb adds two rows per block (512 B).
-        const char* kp = cur + (col & 15) * kKBlock + (col >> 4) * 256 + half * 16;
+        if (j + 1 < nt) dma_tile<D>(nxt, kbase, vbase, tile_key0(j + 1), kmax, uwave, lane);
+        const char* vs = cur + T::kKTileBytes;
+        // K operand: row kb*32 + col, chunk 2*st + half: row col is in block col % NB at
+        // position col / NB; kb adds 32 rows, i.e. 32/NB positions of 2D bytes (512 B).
+        const char* kp = cur + (col % T::kBlocks) * kKBlock + (col / T::kBlocks) * T::kRowBytes + half * 16;
         // V operand rows 16u + trow (+8): block trow (+8), row u inside it.
-        const char* vp = vs + trow * kVBlock + tcol * 2;
+        const char* vp = vs + trow * kVBlock + tcol * 2;   // trow < 8 <= NB: block trow, position 0
 
         // ---- S^T = K Q^T, one 32-key block at a time, all eight K operands read first
         auto scores = [&]() {
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb) {
-                u32x4 ka[8];
+                u32x4 ka[T::kST];
 #pragma unroll
-                for (int st = 0; st < 8; ++st)
+                for (int st = 0; st < T::kST; ++st)
                     ka[st] = *reinterpret_cast<const u32x4*>(kp + kb * 512 + st * 32);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-                for (int st = 0; st < 8; ++st)
+                for (int st = 0; st < T::kST; ++st)
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s[kb],
                                                                    0, 0, 0);
             }
@@ -298,7 +317,7 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
                 mref = nref;
                 lsum *= alpha;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
             }
@@ -339,13 +358,14 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         //      16-lane group, source lane s points at key (s/4) of a four-key set and at
         //      columns 4*(s%4) .. +3 of the group's 16-wide head-dim slice; result lane i
         //      holds column i of that slice for the four keys.
-        u32x4 va[2 * kKB][4];
+        u32x4 va[2 * kKB][T::kDB];
 #pragma unroll
         for (int u = 0; u < 2 * kKB; ++u)
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
+            for (int db = 0; db < T::kDB; ++db) {
+                // row 16u + trow: 16 rows are 16/NB positions of 2D bytes (256 B) further on
                 const u32x2v a0 = lds_read_tr(vp + u * 256 + db * 64);
-                const u32x2v a1 = lds_read_tr(vp + 8 * kVBlock + u * 256 + db * 64);
+                const u32x2v a1 = lds_read_tr(vp + T::kPlus8 + u * 256 + db * 64);
                 va[u][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
             }
 
@@ -359,7 +379,7 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
                 w[i] = pack_bf16x2(s[u >> 1][8 * (u & 1) + 2 * i], s[u >> 1][8 * (u & 1) + 2 * i + 1]);
             const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < T::kDB; ++db)
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[u][db]), pb,
                                                                  acc[db], 0, 0, 0);
         }
@@ -370,7 +390,7 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     };
 
     if (nt > 0) {
-        dma_tile(smem0, kbase, vbase, tile_key0(0), kmax, uwave, lane);
+        dma_tile<D>(smem0, kbase, vbase, tile_key0(0), kmax, uwave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         int j = 0;
@@ -390,7 +410,7 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     if (MODE == 0) {
         uint16_t* op = p.o + hr * kD;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int d0 = db * 32 + gq * 8 + half * 4;
@@ -404,7 +424,7 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         const int64_t out_row = (int64_t)split * p.hq * p.q_rows + hr;
         float* ap = p.a_out + out_row * kD;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int d0 = db * 32 + gq * 8 + half * 4;
@@ -423,23 +443,23 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
 // ------------------------------------------------------------------------- launchers
 
 bool attn_mfma_supported(int d, int hq, int hkv) {
-    if (d != kD || hkv < 1 || hq % hkv) return false;
+    if ((d != 64 && d != 128) || hkv < 1 || hq % hkv) return false;
     const int G = hq / hkv;
     return G >= 1 && G <= kQPB && (kQPB % G) == 0;
 }
 
-int64_t attn_mfma_max_tokens() { return ((int64_t)1 << 31) / kD; }
+int64_t attn_mfma_max_tokens(int d) { return ((int64_t)1 << 31) / d; }
 
 hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               uint16_t* o, float* lse, int64_t L, int64_t block, int64_t anchor,
-                              int hq, int hkv, float scale, hipStream_t stream) {
+                              int hq, int hkv, int d, float scale, hipStream_t stream) {
     AttnMfmaArgs a = {};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
     a.L = L; a.block = block; a.anchor = anchor;
     a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
     a.rows_per_wg = kQPB / a.G;
     a.q_rows = L;
-    a.kv_head_stride = L * kD;
+    a.kv_head_stride = L * d;
     a.scale_log2 = scale * kLog2e;
     const int64_t rw = a.rows_per_wg;
     a.n_blocks = (L + block - 1) / block;
@@ -453,9 +473,11 @@ hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16
     a.tiles_ge1 = tiles_ge1;
     const int64_t tiles = tiles_ge1 + a.nt0;
     const int64_t grid = tiles * hkv;
-    a.head_major = 2.0 * hkv * (double)L * kD * 2 > 256.0 * (1 << 20);
+    a.head_major = 2.0 * hkv * (double)L * d * 2 > 256.0 * (1 << 20);
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_mfma_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    if (d == 128) hipLaunchKernelGGL((attn_mfma_kernel<0, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((attn_mfma_kernel<0, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -492,7 +514,7 @@ int64_t partial_mfma_max_splits(int32_t rows, int32_t hq, int32_t hkv, int n_par
     return (int64_t)partial_splits_wanted(rows, hq, hkv, &nrt) + n_parts;
 }
 
-hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, float scale,
+hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, int d, float scale,
                                const PartPlan& plan, int n_row_tiles, float* a_out, float* m_out,
                                float* l_out, hipStream_t stream) {
     AttnMfmaArgs a = {};
@@ -507,7 +529,9 @@ hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv,
     a.plan = plan;
     const int64_t grid = (int64_t)hkv * n_row_tiles * plan.split_prefix[plan.n_parts];
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    if (d == 128) hipLaunchKernelGGL((attn_mfma_kernel<1, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else if (d == 64) hipLaunchKernelGGL((attn_mfma_kernel<1, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

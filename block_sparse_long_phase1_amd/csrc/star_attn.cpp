@@ -100,12 +100,12 @@ star_status_t star_phase1_encode(const void* q, const void* k, const void* v, vo
             return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
         hipError_t e;
         if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
-            if (L > star::attn_mfma_max_tokens())
+            if (L > star::attn_mfma_max_tokens(d))
                 return fail(STAR_ERR_UNSUPPORTED, "L (%lld) above %lld tokens per kv head", (long long)L,
-                            (long long)star::attn_mfma_max_tokens());
+                            (long long)star::attn_mfma_max_tokens(d));
             e = star::launch_phase1_mfma(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
-                                         L, block, anchor, hq, hkv, scale, stream);
+                                         L, block, anchor, hq, hkv, d, scale, stream);
         } else {
             star::RowAttnArgs a = {};
             a.q = q; a.q_rows = L; a.hq = hq; a.hkv = hkv; a.d = d;
@@ -155,9 +155,9 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
             return fail(STAR_ERR_INVALID_ARG, "pointers and the kv head stride must be 16-byte aligned");
         hipError_t e;
         if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
-            if (n_kv > star::attn_mfma_max_tokens())
+            if (n_kv > star::attn_mfma_max_tokens(d))
                 return fail(STAR_ERR_UNSUPPORTED, "n_kv (%lld) above %lld tokens per partition", (long long)n_kv,
-                            (long long)star::attn_mfma_max_tokens());
+                            (long long)star::attn_mfma_max_tokens(d));
             star::PartPlan plan = {};
             plan.n_parts = 1;
             plan.k[0] = static_cast<const uint16_t*>(k);
@@ -168,7 +168,7 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
             const int nrt = star::partial_mfma_plan(plan, rows, hq, hkv);
             const int32_t ns = plan.split_prefix[1];
             if (ns == 1) {
-                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, scale, plan, nrt,
+                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, d, scale, plan, nrt,
                                               a_out, m_out, l_out, stream);
                 if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
             } else {
@@ -178,7 +178,7 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
                                 need, workspace ? workspace_bytes : (size_t)0);
                 float *wa, *wm, *wl;
                 partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
-                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, scale, plan, nrt,
+                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, d, scale, plan, nrt,
                                               wa, wm, wl, stream);
                 if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
                 e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, a_out, false, nullptr, m_out, l_out, stream);
@@ -235,8 +235,8 @@ star_status_t star_phase2_query(const void* q, int32_t rows, const void* k_ctx, 
         const int64_t causal = tail_len - rows;   // row i sees query-host tokens t <= causal + i
         hipError_t e;
         if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
-            if (L > star::attn_mfma_max_tokens() || tail_cap > star::attn_mfma_max_tokens())
-                return fail(STAR_ERR_UNSUPPORTED, "more than %lld tokens per kv head", (long long)star::attn_mfma_max_tokens());
+            if (L > star::attn_mfma_max_tokens(d) || tail_cap > star::attn_mfma_max_tokens(d))
+                return fail(STAR_ERR_UNSUPPORTED, "more than %lld tokens per kv head", (long long)star::attn_mfma_max_tokens(d));
             star::PartPlan plan = {};
             plan.n_parts = n_shards + 1;
             for (int r = 0; r < n_shards; ++r) {
@@ -261,7 +261,7 @@ star_status_t star_phase2_query(const void* q, int32_t rows, const void* k_ctx, 
                             workspace ? workspace_bytes : (size_t)0);
             float *wa, *wm, *wl;
             partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
-            e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, scale, plan, nrt,
+            e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, d, scale, plan, nrt,
                                           wa, wm, wl, stream);
             if (e != hipSuccess) return hip_fail(e, "star_phase2_query launch");
             e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, o, true, lse, nullptr, nullptr, stream);

@@ -115,11 +115,12 @@ def test_query_validation(lib):
 def test_workspace_queries(lib):
     assert lib.star_phase2_query_workspace_bytes(128, 4, 32, 8, 128) > 0
     assert lib.star_phase2_query_workspace_bytes(128, 0, 32, 8, 128) == 0
-    assert lib.star_phase2_query_workspace_bytes(16, 2, 1, 1, 64) == 0  # vector path needs none
+    assert lib.star_phase2_query_workspace_bytes(16, 2, 1, 1, 96) == 0  # vector path needs none
+    assert lib.star_phase2_query_workspace_bytes(16, 2, 1, 1, 64) > 0   # head dim 64: MFMA path
     assert lib.star_decode_workspace_bytes(32768, 160, 4, 32, 8, 128) > 0
     assert lib.star_decode_workspace_bytes(0, 160, 4, 32, 8, 128) == 0
     assert lib.star_phase2_workspace_bytes(128, 0, 32, 8, 128) == 0
-    assert lib.star_phase2_workspace_bytes(16, 2048, 1, 1, 64) == 0  # vector path needs none
+    assert lib.star_phase2_workspace_bytes(16, 2048, 1, 1, 96) == 0  # vector path needs none
 
 
 def test_binding_names_match_abi():

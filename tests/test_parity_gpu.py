@@ -65,13 +65,33 @@ def test_phase1_f32_tiny(b):
     assert_lse(lse, rl, "LSE", rel=1e-6)
 
 
-def test_phase1_bf16_vector_path_d64():
-    """bf16 with d=64 takes the vector path; same reading, same bar."""
-    cfg = _cfg(4, 2, 300, 128, 128, d=64)
+def test_phase1_bf16_vector_path_d96():
+    """bf16 with a head dim the MFMA kernels do not take (96) uses the vector path; same
+    reading, same bar."""
+    cfg = _cfg(4, 2, 300, 128, 128, d=96)
     q, k, v = sin.phase1_inputs(cfg, DEV)
     o, lse = sa.star_phase1_encode(q, k, v, 128, 128)
     torch.cuda.synchronize()
     ro, rl = oracle.phase1(q.cpu(), k.cpu(), v.cpu(), 128, 128)
+    assert_out(o, ro, "O")
+    assert_lse(lse, rl, "LSE")
+
+
+@pytest.mark.parametrize("hq,hkv,L,b,a", [
+    (4, 2, 300, 128, 128),      # G=2
+    (8, 2, 1000, 320, 200),     # G=4, ragged last block, anchor < block and not tile-aligned
+    (16, 2, 600, 256, 256),     # G=8
+    (2, 2, 500, 200, 200),      # G=1
+    (8, 2, 700, 1024, 1024),    # one block: global causal
+])
+def test_phase1_bf16_d64(hq, hkv, L, b, a):
+    """Head dim 64 on the MFMA kernel (8-row LDS blocks)."""
+    flush_print("phase1 bf16 d64", hq, hkv, L, b, a)
+    cfg = _cfg(hq, hkv, L, b, a, d=64, seed=53)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    o, lse = sa.star_phase1_encode(q, k, v, b, a)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase1(q.cpu(), k.cpu(), v.cpu(), b, a)
     assert_out(o, ro, "O")
     assert_lse(lse, rl, "LSE")
 
@@ -139,14 +159,17 @@ PARTIAL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("hq,hkv,rows,T,lo,hi,off", PARTIAL_CASES)
-def test_phase2_partial_bf16(hq, hkv, rows, T, lo, hi, off):
-    flush_print("partial", hq, hkv, rows, T, lo, hi, off)
+@pytest.mark.parametrize("hq,hkv,rows,T,lo,hi,off,d", [c + (128,) for c in PARTIAL_CASES] + [
+    (8, 2, 100, 3000, 0, 3000, -1, 64),   # head dim 64, several splits
+    (8, 2, 70, 80, 0, 70, 0, 64),         # head dim 64, causal
+])
+def test_phase2_partial_bf16(hq, hkv, rows, T, lo, hi, off, d):
+    flush_print("partial", hq, hkv, rows, T, lo, hi, off, d)
     cfg = _cfg(hq, hkv, T, T, T, seed=11)
-    q = sin.randn(cfg, "q_qry", (hq, rows, 128), DEV)
-    k = sin.randn(cfg, "k_ctx", (hkv, T, 128), DEV)
-    v = sin.randn(cfg, "v_ctx", (hkv, T, 128), DEV)
-    a, m, l = sa.star_phase2_partial(q, k[:, lo:], v[:, lo:], T * 128, hi - lo, off)
+    q = sin.randn(cfg, "q_qry", (hq, rows, d), DEV)
+    k = sin.randn(cfg, "k_ctx", (hkv, T, d), DEV)
+    v = sin.randn(cfg, "v_ctx", (hkv, T, d), DEV)
+    a, m, l = sa.star_phase2_partial(q, k[:, lo:], v[:, lo:], T * d, hi - lo, off)
     torch.cuda.synchronize()
     ra, rm, rl = oracle.partial(q.cpu(), k.cpu(), v.cpu(), lo, hi, off)
     if hi == lo:
@@ -221,6 +244,7 @@ def _run_query_phase(cfg, x, bounds, k_tail, v_tail):
 @pytest.mark.parametrize("hq,hkv,L,b,S,lq,T,dtype,d", [
     (8, 2, 3000, 800, 3, 40, 3, "bf16", 128),
     (16, 2, 1500, 512, 2, 20, 2, "bf16", 128),
+    (8, 2, 1500, 512, 3, 20, 2, "bf16", 64),   # head dim 64: MFMA query, vector-path decode
     (1, 1, 2048, 512, 2, 16, 4, "f32", 64),
 ])
 def test_phase2_query_and_decode(hq, hkv, L, b, S, lq, T, dtype, d):
