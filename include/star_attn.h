@@ -21,9 +21,10 @@
  *   A is normalised over that partition alone, m is the largest scaled score
  *   and l = sum exp(score - m), so the pages' s_h equals e^m * l.  An empty
  *   partition is A = 0, m = -inf, l = 0 and weighs nothing in a merge.
- * Types.  STAR_BF16 inputs are accumulated in fp32 (the fast MFMA kernels
- *   need d = 128); STAR_F32 inputs take a plain vector path (d <= 256, any
- *   multiple of 4).  Partials and LSEs are always fp32.
+ * Types.  STAR_BF16 inputs are accumulated in fp32.  The MFMA kernels take
+ *   d = 64 or 128 for Phase 1 and Phase-2 partials and d = 128 for the decode
+ *   step; other bf16 shapes and STAR_F32 inputs take a plain vector path
+ *   (d <= 256, any multiple of 4).  Partials and LSEs are always fp32.
  * Memory and ownership.  Every pointer not marked "host" is device memory
  *   owned by the caller, 16-byte aligned.  The library never allocates or
  *   frees device memory and keeps no state between calls other than what a
