@@ -31,9 +31,7 @@ namespace star {
 namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kD = 128;
 constexpr int kT = 32;         // keys per tile
-constexpr int kVPitch = 144;   // bf16 per V row in LDS (288 B: 4 consecutive rows hit disjoint banks)
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 struct DecodeArgs {
@@ -80,9 +78,15 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 }  // namespace
 
-template <int G>
+template <int G, int D>
 __global__ void __launch_bounds__(kThreads, 3)
 decode_kernel(const DecodeArgs p) {
+    constexpr int kD = D;                 // head dim, 64 or 128
+    constexpr int kVPitch = D + 16;       // bf16 per V row in LDS: 4 consecutive rows hit disjoint banks
+    constexpr int kDD = D / 32;           // 32-wide head-dim blocks of the S^T products
+    constexpr int kDB = D / 16;           // 16-row blocks of O^T
+    constexpr int kRowChunks = D / 8;     // 16-byte chunks per K/V row
+    constexpr int kVPieces = kT * kRowChunks / 64;   // 16-byte V pieces per lane per tile
     __shared__ __attribute__((aligned(16))) uint16_t vlds[kWaves][kT * kVPitch];
     __shared__ float wm[kWaves][G], wl[kWaves][G];
     __shared__ float wo[kWaves][G][kD];
@@ -114,11 +118,12 @@ decode_kernel(const DecodeArgs p) {
         vb = p.v_tail + (int64_t)g * p.tail_cap * kD;
         if (hi == n_tail) {
             new_key = p.tail_len;
-            // Append the new token's k / v to the query host's cache (32 lanes x 16 B).
-            if (tid < 32) {
-                const uint16_t* src = (tid < 16 ? p.k_new : p.v_new) + (int64_t)g * kD + (tid & 15) * 8;
-                uint16_t* dst = (tid < 16 ? p.k_tail : p.v_tail) + ((int64_t)g * p.tail_cap + p.tail_len) * kD +
-                                (tid & 15) * 8;
+            // Append the new token's k / v to the query host's cache (2 x D/8 lanes x 16 B).
+            if (tid < 2 * kRowChunks) {
+                const bool is_k = tid < kRowChunks;
+                const int c16 = tid % kRowChunks;
+                const uint16_t* src = (is_k ? p.k_new : p.v_new) + (int64_t)g * kD + c16 * 8;
+                uint16_t* dst = (is_k ? p.k_tail : p.v_tail) + ((int64_t)g * p.tail_cap + p.tail_len) * kD + c16 * 8;
                 *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
             }
         }
@@ -128,18 +133,18 @@ decode_kernel(const DecodeArgs p) {
 
     // ---- Q^T as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (grp, col)
     //      holds q head g*G + col (zero past G), head-dim 32*dd + 8*grp .. +7.
-    bf16x8 qb[4];
+    bf16x8 qb[kDD];
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
+    for (int dd = 0; dd < kDD; ++dd) {
         u32x4 w = {0u, 0u, 0u, 0u};
         if (col < G) w = *reinterpret_cast<const u32x4*>(p.q_new + (int64_t)(g * G + col) * kD + dd * 32 + grp * 8);
         qb[dd] = __builtin_bit_cast(bf16x8, w);
     }
 
     // O^T accumulators: head-dim block db of 16 rows; lane (grp, col) holds rows 16db + 4grp + r.
-    f32x4 acc[8];
+    f32x4 acc[kDB];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float mref = kNoMax, lsum = 0.f;
     const float sl2 = p.sl2;
     uint16_t* vt = vlds[wave];
@@ -151,7 +156,7 @@ decode_kernel(const DecodeArgs p) {
     // K operands (16-key block kb, head-dim block dd: key k0 + 16kb + col, head-dim 32dd + 8grp)
     // and V row-major pieces for LDS, for the tile that starts at key k0.  Keys past the chunk
     // are clamped to its last key.
-    u32x4 ka[8], vr[8];
+    u32x4 ka[2 * kDD], vr[kVPieces];
     auto load_tile = [&](int64_t k0) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -159,15 +164,15 @@ decode_kernel(const DecodeArgs p) {
             key = key < hi ? key : hi - 1;
             const uint16_t* src = key == new_key ? knew : kb + key * kD;
 #pragma unroll
-            for (int dd = 0; dd < 4; ++dd) ka[kb2 * 4 + dd] = *reinterpret_cast<const u32x4*>(src + dd * 32 + grp * 8);
+            for (int dd = 0; dd < kDD; ++dd) ka[kb2 * kDD + dd] = *reinterpret_cast<const u32x4*>(src + dd * 32 + grp * 8);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kVPieces; ++i) {
             const int cc = lane + 64 * i;
-            int64_t vkey = k0 + (cc >> 4);
+            int64_t vkey = k0 + cc / kRowChunks;
             vkey = vkey < hi ? vkey : hi - 1;
             const uint16_t* vsrc = vkey == new_key ? vnew : vb + vkey * kD;
-            vr[i] = *reinterpret_cast<const u32x4*>(vsrc + (cc & 15) * 8);
+            vr[i] = *reinterpret_cast<const u32x4*>(vsrc + (cc % kRowChunks) * 8);
         }
     };
     if (wave < n_tiles) load_tile(lo + (int64_t)wave * kT);
@@ -180,14 +185,14 @@ decode_kernel(const DecodeArgs p) {
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             s[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dd = 0; dd < 4; ++dd)
-                s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kb2 * 4 + dd]), qb[dd],
+            for (int dd = 0; dd < kDD; ++dd)
+                s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kb2 * kDD + dd]), qb[dd],
                                                                 s[kb2], 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kVPieces; ++i) {
             const int cc = lane + 64 * i;
-            *reinterpret_cast<u32x4*>(vt + (cc >> 4) * kVPitch + (cc & 15) * 8) = vr[i];
+            *reinterpret_cast<u32x4*>(vt + (cc / kRowChunks) * kVPitch + (cc % kRowChunks) * 8) = vr[i];
         }
         // The operand registers are free again: the next tile's loads fly while this
         // tile's softmax and P.V run.
@@ -213,7 +218,7 @@ decode_kernel(const DecodeArgs p) {
             mref = nref;
             lsum *= alpha;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+            for (int db = 0; db < kDB; ++db) acc[db] *= alpha;
         }
         bf16x8 pb;
         {
@@ -240,7 +245,7 @@ decode_kernel(const DecodeArgs p) {
         // 4*(s%4) .. +3 of the 16-wide head-dim block; result lane i then holds column i of
         // the block for the four keys.  Two reads give the 8 slots.
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        for (int db = 0; db < kDB; ++db) {
             const uint16_t* base = vt + trow * kVPitch + db * 16 + tcol;
             const u32x2v a0 = lds_read_tr(base);
             const u32x2v a1 = lds_read_tr(base + 16 * kVPitch);
@@ -260,7 +265,7 @@ decode_kernel(const DecodeArgs p) {
             wl[wave][col] = lw;
         }
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) wo[wave][col][db * 16 + 4 * grp + r] = acc[db][r];
     }
@@ -298,26 +303,27 @@ decode_kernel(const DecodeArgs p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale cached partials below
     const int nc = pl.n_chunks;
     // One wave per q head, in one pass: lane = (chunk group cg of 16) x (head-dim slice ds
-    // of 32 columns).  Each lane folds chunks cg, cg + 16, ... into a running (m, w, o),
+    // of D/4 columns).  Each lane folds chunks cg, cg + 16, ... into a running (m, w, o),
     // then the 16 chunk groups are folded pairwise across lanes.
     const int cg = lane >> 2, ds = lane & 3;
     for (int q = wave; q < G; q += kWaves) {
         const int h = g * G + q;
         float rm = -INFINITY, rw = 0.f;
-        f32x4 o4[8];
+        constexpr int kSlice4 = D / 16;   // f32x4 per lane: D/4 columns
+        f32x4 o4[kSlice4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kSlice4; ++i) o4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
         for (int ci = cg; ci < nc; ci += 16) {
             const int64_t row = (int64_t)ci * p.hq + h;
             const float m = p.pm[row], l = p.pl[row];
-            const f32x4* src = reinterpret_cast<const f32x4*>(p.pa + row * kD + ds * 32);
+            const f32x4* src = reinterpret_cast<const f32x4*>(p.pa + row * kD + ds * (D / 4));
             const float nm = fmaxf(rm, m);
             const float a = rm == -INFINITY ? 0.f : __expf(rm - nm);
             const float b = m == -INFINITY ? 0.f : l * __expf(m - nm);
             rw = rw * a + b;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o4[i] = o4[i] * a + b * src[i];
+            for (int i = 0; i < kSlice4; ++i) o4[i] = o4[i] * a + b * src[i];
             rm = nm;
         }
 #pragma unroll
@@ -328,7 +334,7 @@ decode_kernel(const DecodeArgs p) {
             const float b = om == -INFINITY ? 0.f : __expf(om - nm);
             rw = rw * a + ow * b;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < kSlice4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o4[i][e] = o4[i][e] * a + __shfl_xor(o4[i][e], sh) * b;
             rm = nm;
@@ -336,15 +342,15 @@ decode_kernel(const DecodeArgs p) {
         const bool empty = rm == -INFINITY || !(rw > 0.f);
         if (cg == 0) {
             const float inv = empty ? 0.f : 1.0f / rw;
-            u32x4 w4[4];
+            u32x4 w4[kSlice4 / 2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kSlice4; ++i) {
                 w4[i >> 1][(i & 1) * 2 + 0] = pack_bf16x2(o4[i][0] * inv, o4[i][1] * inv);
                 w4[i >> 1][(i & 1) * 2 + 1] = pack_bf16x2(o4[i][2] * inv, o4[i][3] * inv);
             }
-            u32x4* dst = reinterpret_cast<u32x4*>(p.o + (int64_t)h * kD + ds * 32);
+            u32x4* dst = reinterpret_cast<u32x4*>(p.o + (int64_t)h * kD + ds * (D / 4));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = w4[i];
+            for (int i = 0; i < kSlice4 / 2; ++i) dst[i] = w4[i];
             if (ds == 0 && p.lse) p.lse[h] = empty ? -INFINITY : rm + __logf(rw);
         }
     }
@@ -353,7 +359,7 @@ decode_kernel(const DecodeArgs p) {
 }
 
 bool decode_bf16_supported(int d, int hq, int hkv) {
-    if (d != kD || hkv < 1 || hq % hkv) return false;
+    if ((d != 64 && d != 128) || hkv < 1 || hq % hkv) return false;
     const int G = hq / hkv;
     return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
 }
@@ -388,7 +394,7 @@ int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv) {
 hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
                               const uint16_t* k_ctx, const uint16_t* v_ctx, int64_t L,
                               uint16_t* k_tail, uint16_t* v_tail, int64_t tail_len, int64_t tail_cap,
-                              int hq, int hkv, float scale, const DecodeChunkPlan& plan,
+                              int hq, int hkv, int d, float scale, const DecodeChunkPlan& plan,
                               float* part_a, float* part_m, float* part_l, unsigned* tickets,
                               uint16_t* o, float* lse, hipStream_t stream) {
     DecodeArgs a;
@@ -404,13 +410,26 @@ hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, cons
     const int64_t grid = (int64_t)hkv * plan.n_chunks;
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 gd((unsigned)grid), bd(kThreads);
-    switch (a.G) {
-        case 1: hipLaunchKernelGGL(decode_kernel<1>, gd, bd, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(decode_kernel<2>, gd, bd, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(decode_kernel<4>, gd, bd, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL(decode_kernel<8>, gd, bd, 0, stream, a); break;
-        case 16: hipLaunchKernelGGL(decode_kernel<16>, gd, bd, 0, stream, a); break;
-        default: return hipErrorInvalidValue;
+    if (d == 128) {
+        switch (a.G) {
+            case 1: hipLaunchKernelGGL((decode_kernel<1, 128>), gd, bd, 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((decode_kernel<2, 128>), gd, bd, 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((decode_kernel<4, 128>), gd, bd, 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_kernel<8, 128>), gd, bd, 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_kernel<16, 128>), gd, bd, 0, stream, a); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (d == 64) {
+        switch (a.G) {
+            case 1: hipLaunchKernelGGL((decode_kernel<1, 64>), gd, bd, 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((decode_kernel<2, 64>), gd, bd, 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((decode_kernel<4, 64>), gd, bd, 0, stream, a); break;
+            case 8: hipLaunchKernelGGL((decode_kernel<8, 64>), gd, bd, 0, stream, a); break;
+            case 16: hipLaunchKernelGGL((decode_kernel<16, 64>), gd, bd, 0, stream, a); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

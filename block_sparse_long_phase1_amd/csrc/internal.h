@@ -73,7 +73,7 @@ hipError_t launch_merge(const float* a, const float* m, const float* l, int n_pa
                         int d, void* o, bool out_bf16, float* lse_out, float* m_out, float* l_out,
                         hipStream_t stream);
 
-// Split-KV decode (bf16, d = 128): chunk partials for every kv head, the append of the
+// Split-KV decode (bf16, d = 64 or 128): chunk partials for every kv head, the append of the
 // new token into the query host's cache, and the log-space merge by the last chunk of
 // each kv head (tickets: hkv zero-initialised counters, left at zero).
 struct DecodeChunkPlan {
@@ -92,7 +92,7 @@ int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv);
 hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
                               const uint16_t* k_ctx, const uint16_t* v_ctx, int64_t L,
                               uint16_t* k_tail, uint16_t* v_tail, int64_t tail_len, int64_t tail_cap,
-                              int hq, int hkv, float scale, const DecodeChunkPlan& plan,
+                              int hq, int hkv, int d, float scale, const DecodeChunkPlan& plan,
                               float* part_a, float* part_m, float* part_l, unsigned* tickets,
                               uint16_t* o, float* lse, hipStream_t stream);
 

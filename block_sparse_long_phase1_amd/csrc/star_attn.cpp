@@ -369,7 +369,7 @@ star_status_t star_decode_step(const void* q_new, const void* k_new, const void*
             e = star::launch_decode_bf16(static_cast<const uint16_t*>(q_new), static_cast<const uint16_t*>(k_new),
                                          static_cast<const uint16_t*>(v_new), static_cast<const uint16_t*>(k_ctx),
                                          static_cast<const uint16_t*>(v_ctx), L, static_cast<uint16_t*>(k_tail),
-                                         static_cast<uint16_t*>(v_tail), tail_len, tail_cap, hq, hkv, scale, plan,
+                                         static_cast<uint16_t*>(v_tail), tail_len, tail_cap, hq, hkv, d, scale, plan,
                                          wa, wm, wl, tickets, static_cast<uint16_t*>(o), lse, stream);
             if (e != hipSuccess) return hip_fail(e, "star_decode_step launch");
         } else {

@@ -244,7 +244,9 @@ def _run_query_phase(cfg, x, bounds, k_tail, v_tail):
 @pytest.mark.parametrize("hq,hkv,L,b,S,lq,T,dtype,d", [
     (8, 2, 3000, 800, 3, 40, 3, "bf16", 128),
     (16, 2, 1500, 512, 2, 20, 2, "bf16", 128),
-    (8, 2, 1500, 512, 3, 20, 2, "bf16", 64),   # head dim 64: MFMA query, vector-path decode
+    (8, 2, 1500, 512, 3, 20, 2, "bf16", 64),   # head dim 64: MFMA query and decode
+    (16, 1, 2333, 700, 4, 5, 3, "bf16", 64),   # d = 64, G = 16, ragged last shard
+    (4, 4, 777, 256, 3, 1, 2, "bf16", 64),     # d = 64, G = 1, one cached query token
     (1, 1, 2048, 512, 2, 16, 4, "f32", 64),
 ])
 def test_phase2_query_and_decode(hq, hkv, L, b, S, lq, T, dtype, d):
@@ -308,13 +310,14 @@ def test_phase2_query_fused(hq, hkv, L, bounds, rows, tail_len, tail_cap):
     assert_lse(lse, rl, "LSE")
 
 
-def test_decode_empty_shard_and_first_token():
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_empty_shard_and_first_token(d):
     """A shard with no tokens weighs nothing; tail_len = 0 is the first cached token."""
-    cfg = _cfg(8, 2, 1000, 250, 250, lq=1, T=1, S=4, seed=29)
+    cfg = _cfg(8, 2, 1000, 250, 250, d=d, lq=1, T=1, S=4, seed=29)
     q, k, v = sin.phase1_inputs(cfg, DEV)
     p2 = sin.phase2_inputs(cfg, DEV)
     bounds = [0, 250, 250, 900, 1000]
-    k_tail = torch.zeros((2, 4, 128), dtype=torch.bfloat16, device=DEV)
+    k_tail = torch.zeros((2, 4, d), dtype=torch.bfloat16, device=DEV)
     v_tail = torch.zeros_like(k_tail)
     o, lse = sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds, k_tail, v_tail, 0)
     torch.cuda.synchronize()
