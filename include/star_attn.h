@@ -22,9 +22,12 @@
  *   and l = sum exp(score - m), so the pages' s_h equals e^m * l.  An empty
  *   partition is A = 0, m = -inf, l = 0 and weighs nothing in a merge.
  * Types.  STAR_BF16 inputs are accumulated in fp32.  The MFMA kernels take
- *   d = 64 or 128 for Phase 1 and Phase-2 partials and d = 128 for the decode
- *   step; other bf16 shapes and STAR_F32 inputs take a plain vector path
+ *   d = 64 or 128 (Phase 1, Phase-2 partials and queries, the decode step);
+ *   other bf16 shapes and STAR_F32 inputs take a plain vector path
  *   (d <= 256, any multiple of 4).  Partials and LSEs are always fp32.
+ * Batches.  B sequences of equal length, laid out [B, H, tokens, d], are one
+ *   call with hq = B*Hq and hkv = B*Hkv: q head b*Hq + h then maps to kv head
+ *   b*Hkv + h/G, which is that sequence's own kv head.
  * Memory and ownership.  Every pointer not marked "host" is device memory
  *   owned by the caller, 16-byte aligned.  The library never allocates or
  *   frees device memory and keeps no state between calls other than what a
@@ -150,7 +153,7 @@ star_status_t star_phase2_partial(const void *q, int32_t rows,
  *   workspace: star_phase2_query_workspace_bytes(rows, n_shards, hq, hkv, d)
  *         bytes (may be 0 for shapes without the MFMA path; then workspace may
  *         be NULL).  Scratch only: its contents need no initialisation.
- * bf16 with d = 128: two kernel launches (the partials of every key split of
+ * bf16 with d = 64 or 128: two kernel launches (the partials of every key split of
  * every partition, then their merge).  Other shapes: one vector-path launch.
  */
 size_t star_phase2_query_workspace_bytes(int32_t rows, int32_t n_shards, int32_t hq, int32_t hkv, int32_t d);
@@ -204,7 +207,7 @@ star_status_t star_softmax_merge(const float *a, const float *m, const float *l,
  *         counters back at zero).  Calls that share a workspace must be
  *         ordered on one stream.
  *   0 <= tail_len < tail_cap.
- * bf16 with d = 128: one kernel launch (chunk partials, the append, and the
+ * bf16 with d = 64 or 128: one kernel launch (chunk partials, the append, and the
  * merge done by the last chunk of each kv head).  Other shapes: an append
  * launch and a vector-path launch.
  */

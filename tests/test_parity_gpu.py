@@ -346,6 +346,46 @@ def test_decode_shard_split_invariance():
         assert (lse - outs[0][1]).abs().max().item() <= 1e-5 * max(1.0, outs[0][1].abs().max().item())
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_batch_as_folded_heads(d):
+    """B equal-length sequences laid out [B, H, tokens, d] are one call with B*Hq q heads and
+    B*Hkv kv heads (q head b*Hq + h maps to kv head b*Hkv + h/G): each sequence's slice of
+    every output matches the oracle run on that sequence alone."""
+    B, hq, hkv, L, b, a, lq, S = 3, 8, 2, 1100, 512, 256, 5, 2
+    flush_print("batch", B, hq, hkv, L, b, a, d)
+    cfgs = [_cfg(hq, hkv, L, b, a, d=d, lq=lq, T=1, S=S, seed=61 + i) for i in range(B)]
+    ins = [sin.phase1_inputs(c, DEV) for c in cfgs]
+    p2s = [sin.phase2_inputs(c, DEV) for c in cfgs]
+    q, k, v = (torch.cat([x[i] for x in ins]) for i in range(3))
+    o, lse = sa.star_phase1_encode(q, k, v, b, a)
+    bounds = shard_bounds(L, b, S)
+    cap = cfgs[0].tail_cap
+    k_tail = torch.zeros((B * hkv, cap, d), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :lq] = torch.cat([p["k_qry"] for p in p2s])
+    v_tail[:, :lq] = torch.cat([p["v_qry"] for p in p2s])
+    qq = torch.cat([p["q_qry"] for p in p2s])
+    oq, lq_lse = sa.star_phase2_query(qq, k, v, bounds, k_tail, v_tail, lq)
+    ws = sa.decode_workspace(L, cap, S, B * hq, B * hkv, d, DEV)
+    od, ld = sa.star_decode_step(torch.cat([p["q_dec"][0] for p in p2s]), torch.cat([p["k_dec"][0] for p in p2s]),
+                                 torch.cat([p["v_dec"][0] for p in p2s]), k, v, bounds, k_tail, v_tail, lq,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(B):
+        qs, ks = slice(i * hq, (i + 1) * hq), slice(i * hkv, (i + 1) * hkv)
+        kc, vc = k[ks].cpu(), v[ks].cpu()
+        ro, rl = oracle.phase1(q[qs].cpu(), kc, vc, b, a)
+        assert_out(o[qs], ro, "phase 1 O, sequence %d" % i)
+        assert_lse(lse[qs], rl, "phase 1 LSE, sequence %d" % i)
+        ro, rl = oracle.phase2_query(qq[qs].cpu(), kc, vc, bounds, p2s[i]["k_qry"].cpu(), p2s[i]["v_qry"].cpu())
+        assert_out(oq[qs], ro, "query O, sequence %d" % i)
+        assert_lse(lq_lse[qs], rl, "query LSE, sequence %d" % i)
+        ro, rl = oracle.phase2_decode(p2s[i]["q_dec"][0].cpu(), kc, vc, bounds, k_tail[ks].cpu(), v_tail[ks].cpu(),
+                                      lq + 1)
+        assert_out(od[qs], ro, "decode O, sequence %d" % i)
+        assert_lse(ld[qs], rl, "decode LSE, sequence %d" % i)
+
+
 def test_decode_steps_replayed_from_a_hip_graph():
     """T decode steps captured in one HIP graph (the library allocates nothing and records no
     memsets) replay bit-identically to the eager calls, with eager work between replays."""
