@@ -15,7 +15,8 @@ aggregation) into the two-phase procedure, in the order the pages give:
 * "NVIDIA/Star-Attention" README (shadowgraph.io mirror), section
   "Two Phases of Star Attention".
 
-bf16 tensors are passed as their uint16 bit patterns; fp32 as float32.
+bf16 tensors are passed as their uint16 bit patterns; fp32 as float32; float64
+arrays (a dequantised fp8 cache, see ``kv_fp8``) as float64.
 """
 from __future__ import annotations
 
@@ -32,7 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "libstar_oracle.so")
 _lib = None
 _lock = threading.Lock()
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -86,7 +87,17 @@ def _as_input(x):
         return x, BF16
     if x.dtype == np.float32:
         return x, F32
-    raise TypeError("oracle inputs must be float32 or uint16 (bf16 bits), got %s" % x.dtype)
+    if x.dtype == np.float64:
+        return x, F64
+    raise TypeError("oracle inputs must be float32, float64 or uint16 (bf16 bits), got %s" % x.dtype)
+
+
+def widen(x) -> np.ndarray:
+    """The exact values of an oracle input (bf16 bits, fp32 or fp64) as float64."""
+    a, dt = _as_input(x)
+    if dt == BF16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def _ptr(a):

@@ -30,10 +30,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
 
 /* Widen one stored element to double.  bf16 is the top half of an IEEE
- * binary32, so the widening is exact. */
+ * binary32, so the widening is exact.  F64 inputs carry values that are
+ * not binary32 numbers (a dequantised cache: scale times a decoded code). */
 static double load_elem(const void *base, int dtype, int64_t idx) {
     if (dtype == ORACLE_BF16) {
         uint16_t h = ((const uint16_t *)base)[idx];
@@ -42,6 +43,7 @@ static double load_elem(const void *base, int dtype, int64_t idx) {
         memcpy(&f, &w, sizeof f);
         return (double)f;
     }
+    if (dtype == ORACLE_F64) return ((const double *)base)[idx];
     return (double)((const float *)base)[idx];
 }
 

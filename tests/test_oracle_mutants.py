@@ -77,3 +77,57 @@ def test_mutant_is_caught(tmp_path, oracle_lib, name):
         oracle._lib = real
     assert caught, "mutant %s passed every pin" % name
     os.remove(so)
+
+
+# ---- the E4M3 context cache (oracle/kv_fp8.py): one slip each, in a private copy of the
+# module, must fail at least one of the pins in test_oracle_fp8.
+FP8_MUTANTS = {
+    "ties_to_odd": ("np.where(lo % 2 == 0, lo, hi)", "np.where(lo % 2 == 1, lo, hi)"),
+    "ties_up": ("np.where(lo % 2 == 0, lo, hi)", "hi"),
+    "overflow_to_nan": ("pick = np.where(a >= E4M3_MAX, 0x7E, pick)", "pick = np.where(a > E4M3_MAX, 0x7F, pick)"),
+    "bias_8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    "subnormal_exponent": ("(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7"),
+    "sign_dropped": ("code = np.where(np.isnan(x), 0x7F, pick) | sign", "code = np.where(np.isnan(x), 0x7F, pick)"),
+    "v_takes_k_scale": ("vd = np.ascontiguousarray(kv_dequantize(v8, v_scale))",
+                        "vd = np.ascontiguousarray(kv_dequantize(v8, k_scale))"),
+    "quantize_multiplies": ("qv = (v / s).astype(np.float32)", "qv = (v * s).astype(np.float32)"),
+    "absmax_over_256": ("s = (amax.astype(np.float32) / np.float32(E4M3_MAX))",
+                        "s = (amax.astype(np.float32) / np.float32(256.0))"),
+}
+
+
+def _fp8_pin_calls():
+    from tests import test_oracle_fp8 as p8
+    return p8, [p8.test_decode_matches_torch_float8_e4m3fn, p8.test_decode_format_values,
+                p8.test_encode_matches_torch_inside_the_finite_range, p8.test_encode_ties_saturation_and_specials,
+                p8.test_encode_round_trips_every_finite_code, p8.test_rounding_error_within_half_a_step,
+                p8.test_absmax_scales_map_each_heads_largest_element_to_448,
+                p8.test_kv8_decode_equals_plain_oracle_on_fp32_exact_values,
+                lambda: p8.test_kv8_decode_against_dense_softmax(None)]
+
+
+def test_fp8_pins_pass_on_the_real_module():
+    _, calls = _fp8_pin_calls()
+    for c in calls:
+        c()
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(monkeypatch, name):
+    import types
+    from oracle import kv_fp8
+    old, new = FP8_MUTANTS[name]
+    src = open(kv_fp8.__file__).read()
+    assert src.count(old) == 1, "mutation site for %s not unique" % name
+    mod = types.ModuleType("oracle.kv_fp8_mutant")
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), "kv_fp8_mutant.py", "exec"), mod.__dict__)
+    p8, calls = _fp8_pin_calls()
+    monkeypatch.setattr(p8, "f8", mod)
+    failed = 0
+    for c in calls:
+        try:
+            c()
+        except Exception:
+            failed += 1
+    assert failed > 0, "mutant %s passed every fp8 pin" % name
