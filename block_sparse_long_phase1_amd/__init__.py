@@ -71,6 +71,13 @@ def load_library(path: str | None = None):
         lib.star_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32, i32,
                                          ctypes.c_int, f32, vp, vp, vp, sz, vp]
         lib.star_decode_step.restype = ctypes.c_int
+        lib.star_kv_fp8_scales.argtypes = [vp, i64, i32, i32, ctypes.c_int, vp, vp]
+        lib.star_kv_fp8_scales.restype = ctypes.c_int
+        lib.star_kv_quantize_fp8.argtypes = [vp, i64, i32, i32, ctypes.c_int, vp, vp, vp]
+        lib.star_kv_quantize_fp8.restype = ctypes.c_int
+        lib.star_decode_step_kv8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32,
+                                             i32, ctypes.c_int, f32, vp, vp, vp, sz, vp]
+        lib.star_decode_step_kv8.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -122,6 +129,16 @@ def _f32(t, name, shape=None):
 def _same(t, ref, name, shape):
     if t.dtype != ref.dtype:
         raise TypeError("%s must be %s, got %s" % (name, ref.dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return _dev(t, name)
+
+
+def _u8(t, name, shape):
+    """uint8 device tensor of the given shape (E4M3 codes)."""
+    torch = _torch()
+    if t.dtype != torch.uint8:
+        raise TypeError("%s must be uint8 (E4M3 codes), got %s" % (name, t.dtype))
     if tuple(t.shape) != tuple(shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
     return _dev(t, name)
@@ -290,9 +307,64 @@ def star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, 
     return o, lse
 
 
+def star_kv_fp8_scales(x, scale=None, stream=None):
+    """Per-kv-head E4M3 scales of a context cache x [Hkv, tokens, d] (bf16 or fp32):
+    max |x[g]| / 448 (1 for an all-zero head), fp32 [Hkv]."""
+    torch = _torch()
+    hkv, n, d = x.shape
+    if scale is None:
+        scale = torch.empty((hkv,), dtype=torch.float32, device=x.device)
+    st = load_library().star_kv_fp8_scales(_dev(x, "x"), n, hkv, d, _dt(x), _f32(scale, "scale", (hkv,)),
+                                           _stream(stream))
+    _check(st, "star_kv_fp8_scales")
+    return scale
+
+
+def star_kv_quantize_fp8(x, scale, out=None, stream=None):
+    """E4M3 codes (uint8 [Hkv, tokens, d]) of x [Hkv, tokens, d] / scale[g]."""
+    torch = _torch()
+    hkv, n, d = x.shape
+    if out is None:
+        out = torch.empty((hkv, n, d), dtype=torch.uint8, device=x.device)
+    st = load_library().star_kv_quantize_fp8(_dev(x, "x"), n, hkv, d, _dt(x), _f32(scale, "scale", (hkv,)),
+                                             _u8(out, "out", (hkv, n, d)), _stream(stream))
+    _check(st, "star_kv_quantize_fp8")
+    return out
+
+
+def star_decode_step_kv8(q_new, k_new, v_new, k_ctx8, v_ctx8, k_scale, v_scale, bounds, k_tail, v_tail,
+                         tail_len: int, o=None, lse=None, workspace=None, scale=None, want_lse: bool = True,
+                         stream=None):
+    """star_decode_step over an E4M3 context cache: k_ctx8/v_ctx8 uint8 [Hkv,L,d] with fp32
+    scales [Hkv]; everything else bf16 as in star_decode_step."""
+    torch = _torch()
+    hq, d = q_new.shape
+    hkv, L, _ = k_ctx8.shape
+    tail_cap = k_tail.shape[1]
+    n_shards = len(bounds) - 1
+    if o is None:
+        o = torch.empty((hq, d), dtype=q_new.dtype, device=q_new.device)
+    if lse is None and want_lse:
+        lse = torch.empty((hq,), dtype=torch.float32, device=q_new.device)
+    if workspace is None:
+        workspace = decode_workspace(L, tail_cap, n_shards, hq, hkv, d, q_new.device)
+    b = (ctypes.c_int64 * (n_shards + 1))(*[int(x) for x in bounds])
+    st = load_library().star_decode_step_kv8(
+        _dev(q_new, "q_new"), _same(k_new, q_new, "k_new", (hkv, d)), _same(v_new, q_new, "v_new", (hkv, d)),
+        _u8(k_ctx8, "k_ctx8", (hkv, L, d)), _u8(v_ctx8, "v_ctx8", (hkv, L, d)),
+        _f32(k_scale, "k_scale", (hkv,)), _f32(v_scale, "v_scale", (hkv,)), L, b, n_shards,
+        _same(k_tail, q_new, "k_tail", (hkv, tail_cap, d)), _same(v_tail, q_new, "v_tail", (hkv, tail_cap, d)),
+        tail_len, tail_cap, hq, hkv, d, _dt(q_new), _scale(d, scale), _same(o, q_new, "o", (hq, d)),
+        ctypes.c_void_p(0) if lse is None else _f32(lse, "lse", (hq,)),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "star_decode_step_kv8")
+    return o, lse
+
+
 __all__ = [
     "CONFIGS", "StarConfig", "n_blocks", "shard_bounds", "load_library", "StarError",
     "star_phase1_encode", "star_phase2_workspace_bytes", "star_phase2_partial", "star_softmax_merge",
     "star_phase2_query_workspace_bytes", "star_phase2_query",
     "star_decode_workspace_bytes", "star_decode_step", "decode_workspace", "STAR_F32", "STAR_BF16",
+    "star_kv_fp8_scales", "star_kv_quantize_fp8", "star_decode_step_kv8",
 ]

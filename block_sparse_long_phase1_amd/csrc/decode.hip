@@ -1,4 +1,4 @@
-// Split-KV grouped-query decode for one generated token (bf16, d = 128).
+// Split-KV grouped-query decode for one generated token (bf16, d = 64 or 128).
 //
 // "Star Attention: Efficient LLM Inference over Long Sequences"
 // (paper-graph-ui summary), section 3.4, Phase 2: each context host computes
@@ -23,6 +23,15 @@
 // (A, m, l) per chunk.  The last workgroup of a kv head to finish (an atomic
 // ticket in the workspace) merges that head's chunk partials in log space and
 // writes the output, then resets its ticket counter to zero.
+//
+// The KV8 instantiations read the context hosts' partitions as E4M3 codes with
+// one scale per kv head for K and for V (kvfp8.hip).  The codes are widened to
+// bf16 in registers with the exact hardware conversion, the K scale is folded
+// into the score scale and the V scale into the chunk's partial, so the tiles,
+// the softmax and the merge are those of the bf16 path.  The query host's
+// partition stays bf16.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -40,6 +49,10 @@ struct DecodeArgs {
     const uint16_t* v_new;
     const uint16_t* k_ctx;
     const uint16_t* v_ctx;
+    const uint8_t* k8;       // E4M3 context cache (KV8 instantiations), else null
+    const uint8_t* v8;
+    const float* k_scale;    // [hkv] scales of k8 / v8
+    const float* v_scale;
     uint16_t* k_tail;
     uint16_t* v_tail;
     int64_t L, tail_len, tail_cap;
@@ -57,6 +70,16 @@ struct DecodeArgs {
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (bytes in memory order) -> eight bf16 (exact: every E4M3 value is a bf16).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    return r;
+}
 
 // Four keys of one head-dim column from a row-major LDS tile (see the kernel comment).
 __device__ __forceinline__ u32x2v lds_read_tr(const uint16_t* p) {
@@ -78,7 +101,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 }  // namespace
 
-template <int G, int D>
+template <int G, int D, bool KV8>
 __global__ void __launch_bounds__(kThreads, 3)
 decode_kernel(const DecodeArgs p) {
     constexpr int kD = D;                 // head dim, 64 or 128
@@ -130,6 +153,10 @@ decode_kernel(const DecodeArgs p) {
     }
     const uint16_t* knew = p.k_new + (int64_t)g * kD;
     const uint16_t* vnew = p.v_new + (int64_t)g * kD;
+    // E4M3 context chunk (uniform over the workgroup)
+    const bool f8 = KV8 && c < pl.chunk_prefix[pl.n_shards];
+    const uint8_t* kb8 = KV8 ? p.k8 + (int64_t)g * p.L * kD : nullptr;
+    const uint8_t* vb8 = KV8 ? p.v8 + (int64_t)g * p.L * kD : nullptr;
 
     // ---- Q^T as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (grp, col)
     //      holds q head g*G + col (zero past G), head-dim 32*dd + 8*grp .. +7.
@@ -146,18 +173,45 @@ decode_kernel(const DecodeArgs p) {
 #pragma unroll
     for (int db = 0; db < kDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float mref = kNoMax, lsum = 0.f;
-    const float sl2 = p.sl2;
     uint16_t* vt = vlds[wave];
     // transposing-read addressing (see the P.V comment below)
     const int trow = 4 * grp + (col >> 2);
     const int tcol = 4 * (col & 3);
 
     const int n_tiles = (int)((hi - lo + kT - 1) / kT);
+    // The tile loop, instantiated for bf16 chunks and (KV8) for E4M3 context chunks.
+    auto run_tiles = [&](auto f8_tag) {
+    constexpr bool F8 = decltype(f8_tag)::value;
+    constexpr int kV8Pieces = kT * kD / 16 / 64;   // 16-byte E4M3 V pieces per lane per tile
+    // score scale (log2 units), with the K scale of an E4M3 chunk folded in
+    const float sl2 = F8 ? p.sl2 * p.k_scale[g] : p.sl2;
     // K operands (16-key block kb, head-dim block dd: key k0 + 16kb + col, head-dim 32dd + 8grp)
     // and V row-major pieces for LDS, for the tile that starts at key k0.  Keys past the chunk
-    // are clamped to its last key.
+    // are clamped to its last key.  E4M3 chunks load half the bytes (ka8, vr8) and widen them
+    // to bf16 when they are used.
     u32x4 ka[2 * kDD], vr[kVPieces];
+    u32x2 ka8[2 * kDD];
+    u32x4 vr8[kV8Pieces];
     auto load_tile = [&](int64_t k0) {
+        if constexpr (F8) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                int64_t key = k0 + 16 * kb2 + col;
+                key = key < hi ? key : hi - 1;
+                const uint8_t* src = kb8 + key * kD;
+#pragma unroll
+                for (int dd = 0; dd < kDD; ++dd)
+                    ka8[kb2 * kDD + dd] = *reinterpret_cast<const u32x2*>(src + dd * 32 + grp * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < kV8Pieces; ++i) {
+                const int cc = lane + 64 * i;
+                int64_t vkey = k0 + cc / (kD / 16);
+                vkey = vkey < hi ? vkey : hi - 1;
+                vr8[i] = *reinterpret_cast<const u32x4*>(vb8 + vkey * kD + (cc % (kD / 16)) * 16);
+            }
+            return;
+        }
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             int64_t key = k0 + 16 * kb2 + col;
@@ -185,14 +239,29 @@ decode_kernel(const DecodeArgs p) {
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             s[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dd = 0; dd < kDD; ++dd)
-                s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kb2 * kDD + dd]), qb[dd],
-                                                                s[kb2], 0, 0, 0);
+            for (int dd = 0; dd < kDD; ++dd) {
+                u32x4 kop;
+                if constexpr (F8)
+                    kop = e4m3x8_to_bf16x8(ka8[kb2 * kDD + dd][0], ka8[kb2 * kDD + dd][1]);
+                else
+                    kop = ka[kb2 * kDD + dd];
+                s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop), qb[dd], s[kb2], 0, 0, 0);
+            }
         }
+        if constexpr (F8) {
 #pragma unroll
-        for (int i = 0; i < kVPieces; ++i) {
-            const int cc = lane + 64 * i;
-            *reinterpret_cast<u32x4*>(vt + (cc / kRowChunks) * kVPitch + (cc % kRowChunks) * 8) = vr[i];
+            for (int i = 0; i < kV8Pieces; ++i) {
+                const int cc = lane + 64 * i;
+                uint16_t* dst = vt + (cc / (kD / 16)) * kVPitch + (cc % (kD / 16)) * 16;
+                *reinterpret_cast<u32x4*>(dst) = e4m3x8_to_bf16x8(vr8[i][0], vr8[i][1]);
+                *reinterpret_cast<u32x4*>(dst + 8) = e4m3x8_to_bf16x8(vr8[i][2], vr8[i][3]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kVPieces; ++i) {
+                const int cc = lane + 64 * i;
+                *reinterpret_cast<u32x4*>(vt + (cc / kRowChunks) * kVPitch + (cc % kRowChunks) * 8) = vr[i];
+            }
         }
         // The operand registers are free again: the next tile's loads fly while this
         // tile's softmax and P.V run.
@@ -256,6 +325,15 @@ decode_kernel(const DecodeArgs p) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    };
+    if constexpr (KV8) {
+        if (f8)
+            run_tiles(std::true_type{});
+        else
+            run_tiles(std::false_type{});
+    } else {
+        run_tiles(std::false_type{});
+    }
 
     // ---- combine the four waves into this chunk's partial
     const float lw = quad_sum(lsum);
@@ -270,6 +348,7 @@ decode_kernel(const DecodeArgs p) {
             for (int r = 0; r < 4; ++r) wo[wave][col][db * 16 + 4 * grp + r] = acc[db][r];
     }
     __syncthreads();
+    const float vsc = (KV8 && f8) ? p.v_scale[g] : 1.0f;   // V scale of an E4M3 chunk
     for (int idx = tid; idx < G * kD; idx += kThreads) {
         const int q = idx / kD, d = idx % kD;
         float M = wm[0][q];
@@ -284,7 +363,8 @@ decode_kernel(const DecodeArgs p) {
         }
         const int64_t prow = (int64_t)c * p.hq + g * G + q;
         // Device-scope stores: they complete at the level that every XCD reads.
-        __hip_atomic_store(p.pa + prow * kD + d, W > 0.f ? o / W : 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.pa + prow * kD + d, W > 0.f ? (o / W) * vsc : 0.f, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0) {
             __hip_atomic_store(p.pm + prow, W > 0.f ? M * kLn2 : -INFINITY, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(p.pl + prow, W > 0.f ? W : 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -391,8 +471,25 @@ int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv) {
     return budget + n_shards + (tail_cap + 127) / 128;
 }
 
+namespace {
+template <int D, bool KV8>
+hipError_t launch_decode_g(const DecodeArgs& a, dim3 gd, hipStream_t stream) {
+    const dim3 bd(kThreads);
+    switch (a.G) {
+        case 1: hipLaunchKernelGGL((decode_kernel<1, D, KV8>), gd, bd, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, D, KV8>), gd, bd, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, D, KV8>), gd, bd, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_kernel<8, D, KV8>), gd, bd, 0, stream, a); break;
+        case 16: hipLaunchKernelGGL((decode_kernel<16, D, KV8>), gd, bd, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
-                              const uint16_t* k_ctx, const uint16_t* v_ctx, int64_t L,
+                              const uint16_t* k_ctx, const uint16_t* v_ctx, const uint8_t* k8, const uint8_t* v8,
+                              const float* k_scale, const float* v_scale, int64_t L,
                               uint16_t* k_tail, uint16_t* v_tail, int64_t tail_len, int64_t tail_cap,
                               int hq, int hkv, int d, float scale, const DecodeChunkPlan& plan,
                               float* part_a, float* part_m, float* part_l, unsigned* tickets,
@@ -400,6 +497,7 @@ hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, cons
     DecodeArgs a;
     a.q_new = q_new; a.k_new = k_new; a.v_new = v_new;
     a.k_ctx = k_ctx; a.v_ctx = v_ctx; a.k_tail = k_tail; a.v_tail = v_tail;
+    a.k8 = k8; a.v8 = v8; a.k_scale = k_scale; a.v_scale = v_scale;
     a.L = L; a.tail_len = tail_len; a.tail_cap = tail_cap;
     a.hq = hq; a.hkv = hkv; a.G = hq / hkv;
     a.sl2 = scale * kLog2e;
@@ -409,29 +507,12 @@ hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, cons
     a.o = o; a.lse = lse;
     const int64_t grid = (int64_t)hkv * plan.n_chunks;
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    const dim3 gd((unsigned)grid), bd(kThreads);
-    if (d == 128) {
-        switch (a.G) {
-            case 1: hipLaunchKernelGGL((decode_kernel<1, 128>), gd, bd, 0, stream, a); break;
-            case 2: hipLaunchKernelGGL((decode_kernel<2, 128>), gd, bd, 0, stream, a); break;
-            case 4: hipLaunchKernelGGL((decode_kernel<4, 128>), gd, bd, 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_kernel<8, 128>), gd, bd, 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_kernel<16, 128>), gd, bd, 0, stream, a); break;
-            default: return hipErrorInvalidValue;
-        }
-    } else if (d == 64) {
-        switch (a.G) {
-            case 1: hipLaunchKernelGGL((decode_kernel<1, 64>), gd, bd, 0, stream, a); break;
-            case 2: hipLaunchKernelGGL((decode_kernel<2, 64>), gd, bd, 0, stream, a); break;
-            case 4: hipLaunchKernelGGL((decode_kernel<4, 64>), gd, bd, 0, stream, a); break;
-            case 8: hipLaunchKernelGGL((decode_kernel<8, 64>), gd, bd, 0, stream, a); break;
-            case 16: hipLaunchKernelGGL((decode_kernel<16, 64>), gd, bd, 0, stream, a); break;
-            default: return hipErrorInvalidValue;
-        }
-    } else {
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    const bool kv8 = k8 != nullptr;
+    if (kv8 && (!v8 || !k_scale || !v_scale)) return hipErrorInvalidValue;
+    const dim3 gd((unsigned)grid);
+    if (d == 128) return kv8 ? launch_decode_g<128, true>(a, gd, stream) : launch_decode_g<128, false>(a, gd, stream);
+    if (d == 64) return kv8 ? launch_decode_g<64, true>(a, gd, stream) : launch_decode_g<64, false>(a, gd, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace star

@@ -89,12 +89,23 @@ bool decode_bf16_supported(int d, int hq, int hkv);
 // call with at most tail_cap query-host tokens and n_shards shards.
 int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv);
 int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv);
+// k8 / v8 non-null: the context partitions are E4M3 codes with per-kv-head scales
+// k_scale / v_scale (k_ctx / v_ctx unused); null: bf16 k_ctx / v_ctx.
 hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
-                              const uint16_t* k_ctx, const uint16_t* v_ctx, int64_t L,
+                              const uint16_t* k_ctx, const uint16_t* v_ctx, const uint8_t* k8, const uint8_t* v8,
+                              const float* k_scale, const float* v_scale, int64_t L,
                               uint16_t* k_tail, uint16_t* v_tail, int64_t tail_len, int64_t tail_cap,
                               int hq, int hkv, int d, float scale, const DecodeChunkPlan& plan,
                               float* part_a, float* part_m, float* part_l, unsigned* tickets,
                               uint16_t* o, float* lse, hipStream_t stream);
+
+// E4M3 context cache (kvfp8.hip).  Both need d % 8 == 0 and 16-byte aligned x.
+// Scales: scale[g] = max |x[g]| / 448 (1 for an all-zero head); three launches.
+hipError_t launch_kv_fp8_scales(const void* x, int64_t tokens, int hkv, int d, bool bf16, float* scale,
+                                hipStream_t stream);
+// out[g] = E4M3 code of x[g] / scale[g] (nearest, ties to even, saturating at 448).
+hipError_t launch_kv_quantize_fp8(const void* x, int64_t tokens, int hkv, int d, bool bf16, const float* scale,
+                                  uint8_t* out, hipStream_t stream);
 
 // Plain vector path (fp32 or bf16 inputs, any d <= 256 with d % 4 == 0): one wave per row.
 struct RowKeySeg {

@@ -62,6 +62,79 @@ void partials_ptrs(void* ws, int64_t n_parts, int64_t n_rows, int32_t d, float**
                                   round_up((size_t)n_parts * n_rows * 4));
 }
 
+// Checks shared by both decode entry points (the context pointers are checked by each).
+star_status_t check_decode(const void* q_new, const void* k_new, const void* v_new, int64_t L,
+                           const int64_t* shard_bounds, int32_t n_shards, const void* k_tail, const void* v_tail,
+                           int64_t tail_len, int64_t tail_cap, int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt,
+                           float scale, const void* o, const float* lse) {
+    if (!q_new || !k_new || !v_new || !k_tail || !v_tail || !o || !shard_bounds)
+        return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+    if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
+    if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
+    if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
+        return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
+    for (int r = 0; r < n_shards; ++r)
+        if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
+    if (tail_len < 0 || tail_cap < 1 || tail_len + 1 > tail_cap)
+        return fail(STAR_ERR_INVALID_ARG, "need 0 <= tail_len < tail_cap (tail_len %lld, tail_cap %lld)",
+                    (long long)tail_len, (long long)tail_cap);
+    if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+    star_status_t s = check_heads(hq, hkv, d, dt);
+    if (s != STAR_OK) return s;
+    if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_tail) || !aligned16(v_tail) ||
+        !aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    return STAR_OK;
+}
+
+// Chunk plan of the decode kernel and its workspace carve-up.
+struct DecodeLaunch {
+    star::DecodeChunkPlan plan;
+    float *a, *m, *l;
+    unsigned* tickets;
+};
+
+star_status_t plan_decode(const int64_t* shard_bounds, int32_t n_shards, int64_t tail_len, int64_t tail_cap,
+                          int32_t hq, int32_t hkv, int32_t d, void* workspace, size_t workspace_bytes,
+                          DecodeLaunch* dl) {
+    star::DecodeChunkPlan& plan = dl->plan;
+    plan = {};
+    plan.n_shards = n_shards;
+    plan.chunk = star::decode_chunk_len(shard_bounds, n_shards, hkv);
+    int64_t nc = 0;
+    for (int r = 0; r < n_shards; ++r) {
+        plan.shard_lo[r] = shard_bounds[r];
+        plan.chunk_prefix[r] = (int32_t)nc;
+        nc += (shard_bounds[r + 1] - shard_bounds[r] + plan.chunk - 1) / plan.chunk;
+    }
+    plan.shard_lo[n_shards] = shard_bounds[n_shards];
+    plan.chunk_prefix[n_shards] = (int32_t)nc;
+    nc += (tail_len + 1 + plan.chunk - 1) / plan.chunk;
+    plan.chunk_prefix[n_shards + 1] = (int32_t)nc;
+    plan.n_chunks = (int32_t)nc;
+    const int64_t n_max = star::decode_max_chunks(tail_cap, n_shards, hkv);
+    if (nc > n_max) return fail(STAR_ERR_HIP, "decode chunk plan exceeds its bound");
+    const size_t part_bytes = partials_bytes(n_max, hq, d);
+    const size_t need = part_bytes + round_up((size_t)hkv * 4);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    partials_ptrs(workspace, n_max, hq, d, &dl->a, &dl->m, &dl->l);
+    dl->tickets = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + part_bytes);
+    return STAR_OK;
+}
+
+star_status_t check_kv_fp8(const void* x, int64_t tokens, int32_t hkv, int32_t d, star_dtype_t dt) {
+    if (!x) return fail(STAR_ERR_INVALID_ARG, "x must be non-null");
+    if (tokens < 0) return fail(STAR_ERR_INVALID_ARG, "tokens (%lld) must be >= 0", (long long)tokens);
+    if (hkv < 1 || hkv > 65535) return fail(STAR_ERR_INVALID_ARG, "hkv (%d) must be in [1, 65535]", hkv);
+    if (dt != STAR_F32 && dt != STAR_BF16) return fail(STAR_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+    if (d < 8 || d > 256 || d % 8)
+        return fail(STAR_ERR_UNSUPPORTED, "head dim %d not supported (need d %% 8 == 0 and 8 <= d <= 256)", d);
+    if (!aligned16(x)) return fail(STAR_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    return STAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,54 +396,22 @@ star_status_t star_decode_step(const void* q_new, const void* k_new, const void*
                                void* o, float* lse, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
     try {
-        if (!q_new || !k_new || !v_new || !k_ctx || !v_ctx || !k_tail || !v_tail || !o || !shard_bounds)
-            return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
-        if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
-        if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
-        if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
-            return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
-        for (int r = 0; r < n_shards; ++r)
-            if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
-        if (tail_len < 0 || tail_cap < 1 || tail_len + 1 > tail_cap)
-            return fail(STAR_ERR_INVALID_ARG, "need 0 <= tail_len < tail_cap (tail_len %lld, tail_cap %lld)",
-                        (long long)tail_len, (long long)tail_cap);
-        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
-        star_status_t s = check_heads(hq, hkv, d, dt);
+        if (!k_ctx || !v_ctx) return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+        if (!aligned16(k_ctx) || !aligned16(v_ctx)) return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+        star_status_t s = check_decode(q_new, k_new, v_new, L, shard_bounds, n_shards, k_tail, v_tail, tail_len,
+                                       tail_cap, hq, hkv, d, dt, scale, o, lse);
         if (s != STAR_OK) return s;
-        if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_ctx) || !aligned16(v_ctx) ||
-            !aligned16(k_tail) || !aligned16(v_tail) || !aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-            return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
         hipError_t e;
         if (dt == STAR_BF16 && star::decode_bf16_supported(d, hq, hkv)) {
-            star::DecodeChunkPlan plan = {};
-            plan.n_shards = n_shards;
-            plan.chunk = star::decode_chunk_len(shard_bounds, n_shards, hkv);
-            int64_t nc = 0;
-            for (int r = 0; r < n_shards; ++r) {
-                plan.shard_lo[r] = shard_bounds[r];
-                plan.chunk_prefix[r] = (int32_t)nc;
-                nc += (shard_bounds[r + 1] - shard_bounds[r] + plan.chunk - 1) / plan.chunk;
-            }
-            plan.shard_lo[n_shards] = shard_bounds[n_shards];
-            plan.chunk_prefix[n_shards] = (int32_t)nc;
-            nc += (tail_len + 1 + plan.chunk - 1) / plan.chunk;
-            plan.chunk_prefix[n_shards + 1] = (int32_t)nc;
-            plan.n_chunks = (int32_t)nc;
-            const int64_t n_max = star::decode_max_chunks(tail_cap, n_shards, hkv);
-            if (nc > n_max) return fail(STAR_ERR_HIP, "star_decode_step: chunk plan exceeds its bound");
-            const size_t part_bytes = partials_bytes(n_max, hq, d);
-            const size_t need = part_bytes + round_up((size_t)hkv * 4);
-            if (!workspace || workspace_bytes < need || !aligned16(workspace))
-                return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
-                            workspace ? workspace_bytes : (size_t)0);
-            float *wa, *wm, *wl;
-            partials_ptrs(workspace, n_max, hq, d, &wa, &wm, &wl);
-            unsigned* tickets = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + part_bytes);
+            DecodeLaunch dl;
+            s = plan_decode(shard_bounds, n_shards, tail_len, tail_cap, hq, hkv, d, workspace, workspace_bytes, &dl);
+            if (s != STAR_OK) return s;
             e = star::launch_decode_bf16(static_cast<const uint16_t*>(q_new), static_cast<const uint16_t*>(k_new),
                                          static_cast<const uint16_t*>(v_new), static_cast<const uint16_t*>(k_ctx),
-                                         static_cast<const uint16_t*>(v_ctx), L, static_cast<uint16_t*>(k_tail),
-                                         static_cast<uint16_t*>(v_tail), tail_len, tail_cap, hq, hkv, d, scale, plan,
-                                         wa, wm, wl, tickets, static_cast<uint16_t*>(o), lse, stream);
+                                         static_cast<const uint16_t*>(v_ctx), nullptr, nullptr, nullptr, nullptr, L,
+                                         static_cast<uint16_t*>(k_tail), static_cast<uint16_t*>(v_tail), tail_len,
+                                         tail_cap, hq, hkv, d, scale, dl.plan, dl.a, dl.m, dl.l, dl.tickets,
+                                         static_cast<uint16_t*>(o), lse, stream);
             if (e != hipSuccess) return hip_fail(e, "star_decode_step launch");
         } else {
             e = star::launch_tail_append(k_new, v_new, k_tail, v_tail, tail_len, tail_cap, hkv, d, elem_bytes(dt), stream);
@@ -390,6 +431,72 @@ star_status_t star_decode_step(const void* q_new, const void* k_new, const void*
         return ok();
     } catch (...) {
         return fail(STAR_ERR_HIP, "star_decode_step: internal error");
+    }
+}
+
+// ------------------------------------------------------------------------ E4M3 context cache
+star_status_t star_kv_fp8_scales(const void* x, int64_t tokens, int32_t hkv, int32_t d, star_dtype_t dt,
+                                 float* scale, hipStream_t stream) {
+    try {
+        star_status_t s = check_kv_fp8(x, tokens, hkv, d, dt);
+        if (s != STAR_OK) return s;
+        if (!scale || (reinterpret_cast<uintptr_t>(scale) & 3u))
+            return fail(STAR_ERR_INVALID_ARG, "scale must be a non-null, 4-byte aligned device pointer");
+        hipError_t e = star::launch_kv_fp8_scales(x, tokens, hkv, d, dt == STAR_BF16, scale, stream);
+        if (e != hipSuccess) return hip_fail(e, "star_kv_fp8_scales launch");
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_kv_fp8_scales: internal error");
+    }
+}
+
+star_status_t star_kv_quantize_fp8(const void* x, int64_t tokens, int32_t hkv, int32_t d, star_dtype_t dt,
+                                   const float* scale, void* out, hipStream_t stream) {
+    try {
+        star_status_t s = check_kv_fp8(x, tokens, hkv, d, dt);
+        if (s != STAR_OK) return s;
+        if (!scale || (reinterpret_cast<uintptr_t>(scale) & 3u))
+            return fail(STAR_ERR_INVALID_ARG, "scale must be a non-null, 4-byte aligned device pointer");
+        if (!out || !aligned16(out)) return fail(STAR_ERR_INVALID_ARG, "out must be a non-null, 16-byte aligned device pointer");
+        hipError_t e = star::launch_kv_quantize_fp8(x, tokens, hkv, d, dt == STAR_BF16, scale,
+                                                    static_cast<uint8_t*>(out), stream);
+        if (e != hipSuccess) return hip_fail(e, "star_kv_quantize_fp8 launch");
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_kv_quantize_fp8: internal error");
+    }
+}
+
+star_status_t star_decode_step_kv8(const void* q_new, const void* k_new, const void* v_new,
+                                   const void* k_ctx8, const void* v_ctx8, const float* k_scale,
+                                   const float* v_scale, int64_t L, const int64_t* shard_bounds, int32_t n_shards,
+                                   void* k_tail, void* v_tail, int64_t tail_len, int64_t tail_cap,
+                                   int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt, float scale,
+                                   void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    try {
+        if (!k_ctx8 || !v_ctx8 || !k_scale || !v_scale) return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+        if (!aligned16(k_ctx8) || !aligned16(v_ctx8) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+            (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+            return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned (scales 4-byte)");
+        star_status_t s = check_decode(q_new, k_new, v_new, L, shard_bounds, n_shards, k_tail, v_tail, tail_len,
+                                       tail_cap, hq, hkv, d, dt, scale, o, lse);
+        if (s != STAR_OK) return s;
+        if (dt != STAR_BF16 || !star::decode_bf16_supported(d, hq, hkv))
+            return fail(STAR_ERR_UNSUPPORTED, "E4M3 context decode needs bf16, d = 64 or 128 and hq/hkv in {1,2,4,8,16}");
+        DecodeLaunch dl;
+        s = plan_decode(shard_bounds, n_shards, tail_len, tail_cap, hq, hkv, d, workspace, workspace_bytes, &dl);
+        if (s != STAR_OK) return s;
+        hipError_t e = star::launch_decode_bf16(
+            static_cast<const uint16_t*>(q_new), static_cast<const uint16_t*>(k_new),
+            static_cast<const uint16_t*>(v_new), nullptr, nullptr, static_cast<const uint8_t*>(k_ctx8),
+            static_cast<const uint8_t*>(v_ctx8), k_scale, v_scale, L, static_cast<uint16_t*>(k_tail),
+            static_cast<uint16_t*>(v_tail), tail_len, tail_cap, hq, hkv, d, scale, dl.plan, dl.a, dl.m, dl.l,
+            dl.tickets, static_cast<uint16_t*>(o), lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "star_decode_step_kv8 launch");
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_decode_step_kv8: internal error");
     }
 }
 

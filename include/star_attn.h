@@ -223,6 +223,63 @@ star_status_t star_decode_step(const void *q_new, const void *k_new, const void 
                                void *o, float *lse,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * E4M3 context KV cache.
+ * [SUM] "Related Work", part "Memory Optimization and KV Cache Compression":
+ * KV-cache quantisation is orthogonal to the method and combines with it.
+ * The pages fix no format; here the context hosts' cached K and V may be held
+ * as OCP E4M3 codes (1 byte per element: sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, largest finite 448, S.1111.111 = NaN) with one fp32 scale
+ * per kv head for K and one for V; the cached value is scale * decode(code).
+ * The query host's cache stays in the compute dtype.  A typical order: Phase
+ * 1, then the query phase on the bf16 cache, then star_kv_fp8_scales and
+ * star_kv_quantize_fp8 on each context tensor, then star_decode_step_kv8 per
+ * generated token.
+ *
+ * star_kv_fp8_scales: scale[g] = max |x[g]| / 448 in fp32 (1 for a head that
+ * is all zeros), so each head's largest element maps to +-448.
+ *   x [hkv, tokens, d] (dt: STAR_BF16 or STAR_F32), 16-byte aligned;
+ *   tokens >= 0; 1 <= hkv <= 65535; d % 8 == 0, 8 <= d <= 256
+ *   scale [hkv] fp32 (device), written.  Three kernel launches, no memset.
+ *
+ * star_kv_quantize_fp8: out[g] = E4M3 code of the correctly rounded fp32
+ * quotient x[g] / scale[g]: the nearest E4M3 value, a tie going to the even
+ * mantissa; magnitudes from 448 up (infinities too) give +-448, NaN gives the
+ * NaN code of its sign.  The sign bit is kept (-0 and negative values that
+ * round to zero give 0x80).
+ *   x as above; scale [hkv] fp32 (device), positive and finite;
+ *   out [hkv, tokens, d] uint8 (device, 16-byte aligned), written.
+ *   One kernel launch.  x and out may not overlap.
+ */
+star_status_t star_kv_fp8_scales(const void *x, int64_t tokens, int32_t hkv, int32_t d,
+                                 star_dtype_t dt, float *scale, hipStream_t stream);
+
+star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32_t hkv, int32_t d,
+                                   star_dtype_t dt, const float *scale, void *out,
+                                   hipStream_t stream);
+
+/*
+ * Phase 2, one generated token over an E4M3 context cache.
+ * [SUM] 3.4 Phase 2 Steps 3-5 and 7 over the dequantised context (see above).
+ *
+ * Arguments and behaviour as star_decode_step, except:
+ *   k_ctx8, v_ctx8 [hkv, L, d] uint8 E4M3 codes (16-byte aligned) replace
+ *   k_ctx / v_ctx; k_scale, v_scale [hkv] fp32 (device) are their scales.
+ *   dt must be STAR_BF16 (q_new, k_new, v_new, the query-host cache and o),
+ *   d 64 or 128 and hq/hkv one of 1, 2, 4, 8, 16; other shapes return
+ *   STAR_ERR_UNSUPPORTED.  The workspace is star_decode_workspace_bytes(...)
+ *   bytes, with the same rules.  One kernel launch.
+ */
+star_status_t star_decode_step_kv8(const void *q_new, const void *k_new, const void *v_new,
+                                   const void *k_ctx8, const void *v_ctx8,
+                                   const float *k_scale, const float *v_scale, int64_t L,
+                                   const int64_t *shard_bounds, int32_t n_shards,
+                                   void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
+                                   int32_t hq, int32_t hkv, int32_t d,
+                                   star_dtype_t dt, float scale,
+                                   void *o, float *lse,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -92,6 +92,38 @@ def test_decode_validation(lib):
     assert d(*args(good, 0, 0, 8, 1 << 30)) == 1                   # no shards
     assert d(*args(good, 65, 0, 8, 1 << 30)) == 1                  # too many shards
     assert d(*args(good, 2, 0, 8, 16)) == 4                        # workspace too small
+
+
+def test_kv_fp8_validation(lib):
+    sc, qz = lib.star_kv_fp8_scales, lib.star_kv_quantize_fp8
+    assert sc(NULL, 100, 8, 128, 1, FAKE, NULL) == 1                     # null x
+    assert sc(FAKE, -1, 8, 128, 1, FAKE, NULL) == 1                      # negative tokens
+    assert sc(FAKE, 100, 0, 128, 1, FAKE, NULL) == 1                     # no heads
+    assert sc(FAKE, 100, 70000, 128, 1, FAKE, NULL) == 1                 # too many heads for the grid
+    assert sc(FAKE, 100, 8, 100, 1, FAKE, NULL) == 2                     # d % 8
+    assert sc(FAKE, 100, 8, 128, 7, FAKE, NULL) == 1                     # bad dtype
+    assert sc(FAKE, 100, 8, 128, 1, NULL, NULL) == 1                     # null scale
+    assert sc(ctypes.c_void_p(0x100008), 100, 8, 128, 1, FAKE, NULL) == 1  # misaligned x
+    assert qz(FAKE, 100, 8, 128, 1, FAKE, NULL, NULL) == 1               # null out
+    assert qz(FAKE, 100, 8, 128, 1, NULL, FAKE, NULL) == 1               # null scale
+    assert qz(FAKE, 100, 8, 128, 1, FAKE, ctypes.c_void_p(0x100008), NULL) == 1  # misaligned out
+
+
+def test_decode_kv8_validation(lib):
+    d = lib.star_decode_step_kv8
+    B = ctypes.c_int64 * 3
+    good = B(0, 50, 100)
+
+    def args(bounds=good, ks=FAKE, hq=4, hkv=2, dim=128, dt=1, tl=0, tc=8, ws=1 << 30):
+        return (FAKE, FAKE, FAKE, FAKE, FAKE, ks, FAKE, 100, bounds, 2, FAKE, FAKE, tl, tc, hq, hkv, dim, dt, 0.1,
+                FAKE, NULL, FAKE, ws, NULL)
+    assert d(*args(ks=NULL)) == 1                          # null scale
+    assert d(*args(bounds=B(0, 60, 50))) == 1              # not monotone
+    assert d(*args(tl=8)) == 1                             # tail full
+    assert d(*args(dt=0)) == 2                             # fp32: no E4M3 path
+    assert d(*args(dim=96)) == 2                           # head dim 96
+    assert d(*args(hq=6, hkv=2)) == 2                      # G = 3
+    assert d(*args(ws=16)) == 4                            # workspace too small
 
 
 def test_query_validation(lib):

@@ -1,0 +1,177 @@
+"""GPU parity of the E4M3 context cache: scales and codes bit-exact against the oracle, and
+the decode step over an E4M3 context (codes and scales made by the oracle) against the
+oracle's decode over the dequantised values."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_phase1_amd as sa
+import oracle
+from oracle import kv_fp8 as of8
+from block_sparse_long_phase1_amd import inputs as sin
+from block_sparse_long_phase1_amd.configs import CONFIGS, StarConfig, shard_bounds
+from tests._parity import assert_lse, assert_out, flush_print
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _cfg(hq, hkv, L, b, d=128, dtype="bf16", lq=16, T=3, S=2, seed=71):
+    return StarConfig("test", hq=hq, hkv=hkv, d=d, L=L, block=b, anchor=b, lq=lq, decode_steps=T,
+                      shards=S, dtype=dtype, needle=False, seed=seed)
+
+
+def _oracle_cache(k, v):
+    """Scales and E4M3 codes of k, v [Hkv, L, d] made by the oracle, on the device."""
+    ks, vs = of8.kv_absmax_scales(k.cpu()), of8.kv_absmax_scales(v.cpu())
+    k8 = np.stack([of8.kv_quantize(k[g:g + 1].cpu(), ks[g:g + 1])[0] for g in range(k.shape[0])])
+    v8 = np.stack([of8.kv_quantize(v[g:g + 1].cpu(), vs[g:g + 1])[0] for g in range(v.shape[0])])
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return to(k8), to(v8), to(ks), to(vs), (k8, v8, ks, vs)
+
+
+@pytest.mark.parametrize("hkv,L,d,dtype", [(3, 1000, 128, "bf16"), (2, 777, 64, "bf16"), (3, 300, 64, "f32"),
+                                           (1, 1, 8, "f32")])
+def test_scales_and_codes_bit_exact(hkv, L, d, dtype):
+    flush_print("kv fp8 codes", hkv, L, d, dtype)
+    cfg = _cfg(hkv, hkv, L, L, d=d, dtype=dtype, seed=73)
+    x = sin.randn(cfg, "k_ctx", (hkv, L, d), DEV) * 3.0
+    if hkv == 3:
+        x[1].zero_()                     # an all-zero head takes scale 1
+    s = sa.star_kv_fp8_scales(x)
+    c = sa.star_kv_quantize_fp8(x, s)
+    torch.cuda.synchronize()
+    rs = of8.kv_absmax_scales(x.cpu())
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32)), (s.cpu().numpy(), rs)
+    rc = of8.kv_quantize(x.cpu(), rs)
+    got = c.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, "%d codes differ, first at %s: %s vs %s" % (
+        len(bad), bad[0], got[tuple(bad[0])], rc[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_codes_at_format_edges(dtype):
+    """Every finite E4M3 value, every midpoint between neighbours (exact ties), the fp32
+    neighbours of each midpoint, saturation, infinities, NaN and signed zeros, with scale 1."""
+    mags = of8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (mags[:-1] + mags[1:]) / 2
+    vals = [mags, mids, [448.0, 450.0, 464.0, 500.0, 2.0 ** 100, np.inf, 2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -10]]
+    if dtype == "f32":
+        m32 = mids.astype(np.float32)
+        vals += [np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9))]
+    x = np.concatenate([np.asarray(v, np.float64) for v in vals]).astype(np.float32)
+    x = np.concatenate([x, -x, np.float32([np.nan, -np.nan, 0.0, -0.0])])
+    x = np.concatenate([x, np.zeros((-x.size) % 8, np.float32)]).reshape(1, -1, 8)
+    t = torch.from_numpy(x)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+        assert np.array_equal(t.float().numpy()[np.isfinite(x)], x[np.isfinite(x)])   # all exact in bf16
+    t = t.to(DEV)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    c = sa.star_kv_quantize_fp8(t, one)
+    torch.cuda.synchronize()
+    rc = of8.kv_quantize(t.cpu(), np.float32([1.0]))
+    got = c.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, [(float(x[tuple(i)]), hex(got[tuple(i)]), hex(rc[tuple(i)])) for i in bad[:8]]
+
+
+@pytest.mark.parametrize("hq,hkv,L,bounds,lq,T,d", [
+    (8, 2, 3000, [0, 800, 1600, 3000], 40, 3, 128),         # G = 4, ragged shards
+    (16, 1, 2333, [0, 700, 700, 2333], 5, 3, 64),           # d = 64, G = 16, an empty shard
+    (4, 4, 777, [0, 777], 1, 2, 128),                        # G = 1, one cached query token
+    (16, 2, 1500, [0, 512, 1024, 1500], 20, 2, 128),        # G = 8
+    (4, 2, 600, [0, 100, 600], 0, 2, 64),                    # G = 2, first token is the first cached one
+])
+def test_decode_kv8(hq, hkv, L, bounds, lq, T, d):
+    flush_print("decode kv8", hq, hkv, L, bounds, lq, T, d)
+    cfg = _cfg(hq, hkv, L, L, d=d, lq=max(lq, 1), T=T, S=len(bounds) - 1, seed=79)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    k8, v8, ks, vs, (hk8, hv8, hks, hvs) = _oracle_cache(k, v)
+    k_tail = torch.zeros((hkv, lq + T, d), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :lq] = p2["k_qry"][:, :lq]
+    v_tail[:, :lq] = p2["v_qry"][:, :lq]
+    ws = sa.decode_workspace(L, lq + T, len(bounds) - 1, hq, hkv, d, DEV)
+    for t in range(T):
+        o, lse = sa.star_decode_step_kv8(p2["q_dec"][t], p2["k_dec"][t], p2["v_dec"][t], k8, v8, ks, vs, bounds,
+                                         k_tail, v_tail, lq + t, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(k_tail[:, lq + t], p2["k_dec"][t]) and torch.equal(v_tail[:, lq + t], p2["v_dec"][t])
+        ro, rl = of8.phase2_decode_kv8(p2["q_dec"][t].cpu(), hk8, hv8, hks, hvs, bounds, k_tail.cpu(),
+                                       v_tail.cpu(), lq + t + 1)
+        assert_out(o, ro, "kv8 decode O step %d" % t)
+        assert_lse(lse, rl, "kv8 decode LSE step %d" % t)
+
+
+def test_decode_kv8_equals_bf16_decode_on_representable_values():
+    """With unit scales and a context whose bf16 values are E4M3 values, the E4M3 decode step
+    and the bf16 decode step compute the same numbers: their outputs are bit-identical."""
+    cfg = _cfg(8, 2, 2000, 2000, lq=8, T=1, S=2, seed=83)
+    _, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    one = np.float32([1.0, 1.0])
+    hk8 = of8.kv_quantize(k.cpu(), one)
+    hv8 = of8.kv_quantize(v.cpu(), one)
+    kr = torch.from_numpy(of8.e4m3_decode(hk8).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    vr = torch.from_numpy(of8.e4m3_decode(hv8).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    bounds = [0, 900, 2000]
+    outs = []
+    for kv8 in (False, True):
+        kt = torch.zeros((2, 9, 128), dtype=torch.bfloat16, device=DEV)
+        vt = torch.zeros_like(kt)
+        kt[:, :8] = p2["k_qry"]
+        vt[:, :8] = p2["v_qry"]
+        if kv8:
+            ones = torch.ones(2, dtype=torch.float32, device=DEV)
+            o, l = sa.star_decode_step_kv8(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0],
+                                           torch.from_numpy(hk8).to(DEV), torch.from_numpy(hv8).to(DEV), ones, ones,
+                                           bounds, kt, vt, 8)
+        else:
+            o, l = sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], kr, vr, bounds, kt, vt, 8)
+        outs.append((o, l))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.timeout(400)
+def test_decode_kv8_full_8b_32k():
+    """The 8b_32k workload (Hq=32, Hkv=8, d=128, L=32768, 4 shards) at full size: the GPU's
+    scales and codes of the whole context equal the oracle's, and the first and last of T
+    decode steps over the oracle-made E4M3 cache match the oracle."""
+    cfg = CONFIGS["8b_32k"]
+    flush_print("kv8 full", cfg.name)
+    x = sin.all_inputs(cfg, DEV)
+    k, v = x["k_ctx"], x["v_ctx"]
+    bounds = cfg.bounds()
+    k8, v8, ks, vs, (hk8, hv8, hks, hvs) = _oracle_cache(k, v)
+    flush_print("  oracle cache made")
+    gks = sa.star_kv_fp8_scales(k)
+    gk8 = sa.star_kv_quantize_fp8(k, gks)
+    gvs = sa.star_kv_fp8_scales(v)
+    gv8 = sa.star_kv_quantize_fp8(v, gvs)
+    torch.cuda.synchronize()
+    assert torch.equal(gks, ks) and torch.equal(gvs, vs)
+    assert torch.equal(gk8, k8) and torch.equal(gv8, v8)
+    del gk8, gv8
+    k_tail = torch.zeros((cfg.hkv, cfg.tail_cap, cfg.d), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :cfg.lq] = x["k_qry"]
+    v_tail[:, :cfg.lq] = x["v_qry"]
+    T = cfg.decode_steps
+    ws = sa.decode_workspace(cfg.L, cfg.tail_cap, cfg.shards, cfg.hq, cfg.hkv, cfg.d, DEV)
+    od = torch.empty((T, cfg.hq, cfg.d), dtype=torch.bfloat16, device=DEV)
+    ld = torch.empty((T, cfg.hq), dtype=torch.float32, device=DEV)
+    for t in range(T):
+        sa.star_decode_step_kv8(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k8, v8, ks, vs, bounds, k_tail, v_tail,
+                                cfg.lq + t, o=od[t], lse=ld[t], workspace=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(ld).all())
+    kt, vt = k_tail.cpu(), v_tail.cpu()
+    for t in (0, T - 1):
+        ro, rl = of8.phase2_decode_kv8(x["q_dec"][t].cpu(), hk8, hv8, hks, hvs, bounds, kt, vt, cfg.lq + t + 1)
+        assert_out(od[t], ro, "8b_32k kv8 decode step %d O" % t)
+        assert_lse(ld[t], rl, "8b_32k kv8 decode step %d LSE" % t)
+    flush_print("  kv8 decode ok")
