@@ -12,8 +12,10 @@ Prints ONE JSON line.  `value` is context tokens per second of the whole step
 algorithmic flops per launch / its average launch time measured with HIP events on the
 launch stream, against the bf16 dense MFMA peak.  `decode` reports the decode step's
 K/V stream rate (warm: inside the step; cold: after overwriting 1 GiB and reading it back,
-so the 256 MB last-level cache holds no K/V and no dirty lines).  `cpu_baseline` times the fp64 oracle on a bounded sample
-of Phase-1 rows on the host's cores.
+so the 256 MB last-level cache holds no K/V and no dirty lines).  `decode_kv8` reports the
+same decode steps over an E4M3 context cache (quantised once, after the step; its time is
+reported too) against the same bytes model with 1-byte context elements.  `cpu_baseline`
+times the fp64 oracle on a bounded sample of Phase-1 rows on the host's cores.
 """
 from __future__ import annotations
 
@@ -70,6 +72,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-reps", type=int, default=8)
+    ap.add_argument("--no-kv8", action="store_true", help="skip the E4M3 context-cache decode leg")
     ap.add_argument("--only", choices=["all", "phase1", "decode"], default="all",
                     help="restrict the timed step (for profiling runs); the JSON line is always the full step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -206,6 +209,68 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         cold.append((a.elapsed_time(b), cfg.decode_step_bytes(t)))
+
+    # ---- E4M3 context cache: quantise the context once, then the decode steps over it
+    kv8 = None
+    if cfg.dtype == "bf16" and not args.no_kv8:
+        ks = torch.empty((cfg.hkv,), dtype=torch.float32, device=dev)
+        vs = torch.empty_like(ks)
+        k8 = torch.empty((cfg.hkv, cfg.L, cfg.d), dtype=torch.uint8, device=dev)
+        v8 = torch.empty_like(k8)
+
+        def quantize():
+            sa.star_kv_fp8_scales(k, ks, stream=stream)
+            sa.star_kv_quantize_fp8(k, ks, k8, stream=stream)
+            sa.star_kv_fp8_scales(v, vs, stream=stream)
+            sa.star_kv_quantize_fp8(v, vs, v8, stream=stream)
+
+        def decode8(t):
+            sa.star_decode_step_kv8(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k8, v8, ks, vs, bounds, k_tail,
+                                    v_tail, cfg.lq + t, o=od[t], lse=ld[t], workspace=ws_dec, stream=stream)
+
+        quantize()
+        qz = []
+        for _ in range(3):
+            a, b = ev(), ev()
+            a.record(stream)
+            quantize()
+            b.record(stream)
+            qz.append((a, b))
+        for _ in range(args.warmup):
+            for t in range(cfg.decode_steps):
+                decode8(t)
+        reps = []
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            for t in range(cfg.decode_steps):
+                decode8(t)
+            b.record(stream)
+            reps.append((a, b))
+        torch.cuda.synchronize()
+        q8_ms = float(np.mean([a.elapsed_time(b) for a, b in qz]))
+        d8_ms = float(np.mean([a.elapsed_time(b) for a, b in reps]))
+        cold8 = []
+        for r in range(args.cold_reps):
+            flush.fill_(float(r))
+            torch.sum(flush, dim=0, out=sink)
+            t = r % cfg.decode_steps
+            a, b = ev(), ev()
+            a.record(stream)
+            decode8(t)
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold8.append((a.elapsed_time(b), cfg.decode_step_bytes_kv8(t)))
+        b8 = sum(cfg.decode_step_bytes_kv8(t) for t in range(cfg.decode_steps))
+        w8 = b8 / (d8_ms * 1e-3)
+        c8 = sum(bb for _, bb in cold8) / (sum(ms for ms, _ in cold8) * 1e-3)
+        qbytes = 2 * cfg.hkv * cfg.L * cfg.d * (2 * 2 + 1)   # two reads of bf16 K and V, one E4M3 write
+        kv8 = {"ms_per_token": d8_ms / cfg.decode_steps, "bytes_per_token": b8 / cfg.decode_steps,
+               "warm_GBps": w8 / 1e9, "warm_hbm_frac": w8 / PEAK_HBM_BYTES,
+               "cold_GBps": c8 / 1e9, "cold_hbm_frac": c8 / PEAK_HBM_BYTES,
+               "cold_ms_per_token": float(np.mean([ms for ms, _ in cold8])),
+               "quantize_ms": q8_ms, "quantize_GBps": qbytes / (q8_ms * 1e-3) / 1e9}
+        del k8, v8
     del flush
 
     flops = cfg.phase1_flops()
@@ -246,6 +311,7 @@ def main():
                    "warm_GBps": warm_bw / 1e9, "warm_hbm_frac": warm_bw / PEAK_HBM_BYTES,
                    "cold_GBps": cold_bw / 1e9, "cold_hbm_frac": cold_bw / PEAK_HBM_BYTES,
                    "cold_ms_per_token": float(np.mean([ms for ms, _ in cold]))},
+        "decode_kv8": kv8,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -101,6 +101,12 @@ class StarConfig:
         eb = 2 if self.dtype == "bf16" else 4
         return 2 * self.hkv * (self.L + self.lq + t + 1) * self.d * eb
 
+    def decode_step_bytes_kv8(self, t: int) -> int:
+        """The same with an E4M3 context cache (1 byte per element) and the query host's
+        cache in the compute dtype."""
+        eb = 2 if self.dtype == "bf16" else 4
+        return 2 * self.hkv * self.d * (self.L + (self.lq + t + 1) * eb)
+
 
 _BASE_SEED = 20241126
 

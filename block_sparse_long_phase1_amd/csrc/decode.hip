@@ -81,6 +81,19 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     return r;
 }
 
+// One tile's operand registers: K (the A operands of S^T) and the V pieces bound for LDS,
+// as bf16 or as E4M3 codes (half the bytes).
+template <int NK, int NV>
+struct TileBf16 {
+    u32x4 k[NK];
+    u32x4 v[NV];
+};
+template <int NK, int NV>
+struct TileE4m3 {
+    u32x2 k[NK];
+    u32x4 v[NV];
+};
+
 // Four keys of one head-dim column from a row-major LDS tile (see the kernel comment).
 __device__ __forceinline__ u32x2v lds_read_tr(const uint16_t* p) {
     lds_bf16x4* lp = (lds_bf16x4*)((__attribute__((address_space(3))) uint16_t*)(const_cast<uint16_t*>(p)));
@@ -187,12 +200,13 @@ decode_kernel(const DecodeArgs p) {
     const float sl2 = F8 ? p.sl2 * p.k_scale[g] : p.sl2;
     // K operands (16-key block kb, head-dim block dd: key k0 + 16kb + col, head-dim 32dd + 8grp)
     // and V row-major pieces for LDS, for the tile that starts at key k0.  Keys past the chunk
-    // are clamped to its last key.  E4M3 chunks load half the bytes (ka8, vr8) and widen them
-    // to bf16 when they are used.
-    u32x4 ka[2 * kDD], vr[kVPieces];
-    u32x2 ka8[2 * kDD];
-    u32x4 vr8[kV8Pieces];
-    auto load_tile = [&](int64_t k0) {
+    // are clamped to its last key.  E4M3 chunks load half the bytes and widen them to bf16
+    // when they are used; a wave keeps two of their tiles in flight (kDepth), so that it
+    // has as many bytes outstanding as with one bf16 tile.
+    using Tile = typename std::conditional<F8, TileE4m3<2 * kDD, kV8Pieces>, TileBf16<2 * kDD, kVPieces>>::type;
+    constexpr int kDepth = F8 ? 2 : 1;
+    Tile buf[kDepth];
+    auto load_tile = [&](Tile& b, int64_t k0) {
         if constexpr (F8) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -201,24 +215,23 @@ decode_kernel(const DecodeArgs p) {
                 const uint8_t* src = kb8 + key * kD;
 #pragma unroll
                 for (int dd = 0; dd < kDD; ++dd)
-                    ka8[kb2 * kDD + dd] = *reinterpret_cast<const u32x2*>(src + dd * 32 + grp * 8);
+                    b.k[kb2 * kDD + dd] = *reinterpret_cast<const u32x2*>(src + dd * 32 + grp * 8);
             }
 #pragma unroll
             for (int i = 0; i < kV8Pieces; ++i) {
                 const int cc = lane + 64 * i;
                 int64_t vkey = k0 + cc / (kD / 16);
                 vkey = vkey < hi ? vkey : hi - 1;
-                vr8[i] = *reinterpret_cast<const u32x4*>(vb8 + vkey * kD + (cc % (kD / 16)) * 16);
+                b.v[i] = *reinterpret_cast<const u32x4*>(vb8 + vkey * kD + (cc % (kD / 16)) * 16);
             }
-            return;
-        }
+        } else {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             int64_t key = k0 + 16 * kb2 + col;
             key = key < hi ? key : hi - 1;
             const uint16_t* src = key == new_key ? knew : kb + key * kD;
 #pragma unroll
-            for (int dd = 0; dd < kDD; ++dd) ka[kb2 * kDD + dd] = *reinterpret_cast<const u32x4*>(src + dd * 32 + grp * 8);
+            for (int dd = 0; dd < kDD; ++dd) b.k[kb2 * kDD + dd] = *reinterpret_cast<const u32x4*>(src + dd * 32 + grp * 8);
         }
 #pragma unroll
         for (int i = 0; i < kVPieces; ++i) {
@@ -226,11 +239,13 @@ decode_kernel(const DecodeArgs p) {
             int64_t vkey = k0 + cc / kRowChunks;
             vkey = vkey < hi ? vkey : hi - 1;
             const uint16_t* vsrc = vkey == new_key ? vnew : vb + vkey * kD;
-            vr[i] = *reinterpret_cast<const u32x4*>(vsrc + (cc % kRowChunks) * 8);
+            b.v[i] = *reinterpret_cast<const u32x4*>(vsrc + (cc % kRowChunks) * 8);
+        }
         }
     };
-    if (wave < n_tiles) load_tile(lo + (int64_t)wave * kT);
-    for (int t = wave; t < n_tiles; t += kWaves) {
+    // One tile of this wave: S^T from b, V from b into LDS, then b takes the load of the
+    // tile kDepth steps ahead while the softmax and P.V of this one run.
+    auto tile_body = [&](Tile& b, int t) {
         const int64_t k0 = lo + (int64_t)t * kT;
         // S^T = K Q^T: s[kb][r] is key k0 + 16kb + 4grp + r for q column col; and this tile's V
         // into the wave's LDS tile
@@ -242,9 +257,9 @@ decode_kernel(const DecodeArgs p) {
             for (int dd = 0; dd < kDD; ++dd) {
                 u32x4 kop;
                 if constexpr (F8)
-                    kop = e4m3x8_to_bf16x8(ka8[kb2 * kDD + dd][0], ka8[kb2 * kDD + dd][1]);
+                    kop = e4m3x8_to_bf16x8(b.k[kb2 * kDD + dd][0], b.k[kb2 * kDD + dd][1]);
                 else
-                    kop = ka[kb2 * kDD + dd];
+                    kop = b.k[kb2 * kDD + dd];
                 s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop), qb[dd], s[kb2], 0, 0, 0);
             }
         }
@@ -253,20 +268,20 @@ decode_kernel(const DecodeArgs p) {
             for (int i = 0; i < kV8Pieces; ++i) {
                 const int cc = lane + 64 * i;
                 uint16_t* dst = vt + (cc / (kD / 16)) * kVPitch + (cc % (kD / 16)) * 16;
-                *reinterpret_cast<u32x4*>(dst) = e4m3x8_to_bf16x8(vr8[i][0], vr8[i][1]);
-                *reinterpret_cast<u32x4*>(dst + 8) = e4m3x8_to_bf16x8(vr8[i][2], vr8[i][3]);
+                *reinterpret_cast<u32x4*>(dst) = e4m3x8_to_bf16x8(b.v[i][0], b.v[i][1]);
+                *reinterpret_cast<u32x4*>(dst + 8) = e4m3x8_to_bf16x8(b.v[i][2], b.v[i][3]);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kVPieces; ++i) {
                 const int cc = lane + 64 * i;
-                *reinterpret_cast<u32x4*>(vt + (cc / kRowChunks) * kVPitch + (cc % kRowChunks) * 8) = vr[i];
+                *reinterpret_cast<u32x4*>(vt + (cc / kRowChunks) * kVPitch + (cc % kRowChunks) * 8) = b.v[i];
             }
         }
         // The operand registers are free again: the next tile's loads fly while this
         // tile's softmax and P.V run.
         __builtin_amdgcn_sched_barrier(0);
-        if (t + kWaves < n_tiles) load_tile(k0 + (int64_t)kWaves * kT);
+        if (t + kDepth * kWaves < n_tiles) load_tile(b, k0 + (int64_t)kDepth * kWaves * kT);
         __builtin_amdgcn_sched_barrier(0);
         if (k0 + kT > hi) {
             const int lim = (int)(hi - k0);
@@ -324,6 +339,14 @@ decode_kernel(const DecodeArgs p) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j)
+        if (wave + j * kWaves < n_tiles) load_tile(buf[j], lo + (int64_t)(wave + j * kWaves) * kT);
+    for (int t = wave; t < n_tiles; t += kDepth * kWaves) {
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j)
+            if (t + j * kWaves < n_tiles) tile_body(buf[j], t + j * kWaves);
     }
     };
     if constexpr (KV8) {
