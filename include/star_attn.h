@@ -11,7 +11,7 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Layout.  Batch 1, head-major, contiguous: queries [Hq, rows, d], keys and
+ * Layout.  One sequence (see Batches below), head-major, contiguous: queries [Hq, rows, d], keys and
  *   values [Hkv, tokens, d].  Grouped-query attention maps q head h to kv
  *   head h / (Hq / Hkv) (contiguous groups).  Hq must be a multiple of Hkv.
  * Scale.  Scores are scale * <q, k>; pass scale = 1/sqrt(d) for the pages'
