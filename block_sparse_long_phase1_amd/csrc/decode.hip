@@ -405,57 +405,65 @@ decode_kernel(const DecodeArgs p) {
     if (ticket_sh != (unsigned)(pl.n_chunks - 1)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale cached partials below
     const int nc = pl.n_chunks;
-    // One wave per q head, in one pass: lane = (chunk group cg of 16) x (head-dim slice ds
-    // of D/4 columns).  Each lane folds chunks cg, cg + 16, ... into a running (m, w, o),
-    // then the 16 chunk groups are folded pairwise across lanes.
-    const int cg = lane >> 2, ds = lane & 3;
+    // One wave per q head.  The chunks are taken in batches of 64 / (D/64), and every load of
+    // a batch is issued at once (one memory round trip): lane i loads the statistics (m, l) of
+    // chunk c0 + i, and every lane loads its D/64 head-dim columns of every chunk of the
+    // batch.  The wave then forms the batch max and weights and folds the weighted columns,
+    // rescaling what earlier batches left when the max grows.
+    constexpr int kCols = D / 64;
+    constexpr int kBatch = 64 / kCols;   // 64 registers of columns per lane
     for (int q = wave; q < G; q += kWaves) {
         const int h = g * G + q;
-        float rm = -INFINITY, rw = 0.f;
-        constexpr int kSlice4 = D / 16;   // f32x4 per lane: D/4 columns
-        f32x4 o4[kSlice4];
+        float M = -INFINITY, W = 0.f;
+        float o[kCols];
 #pragma unroll
-        for (int i = 0; i < kSlice4; ++i) o4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int ci = cg; ci < nc; ci += 16) {
-            const int64_t row = (int64_t)ci * p.hq + h;
-            const float m = p.pm[row], l = p.pl[row];
-            const f32x4* src = reinterpret_cast<const f32x4*>(p.pa + row * kD + ds * (D / 4));
-            const float nm = fmaxf(rm, m);
-            const float a = rm == -INFINITY ? 0.f : __expf(rm - nm);
-            const float b = m == -INFINITY ? 0.f : l * __expf(m - nm);
-            rw = rw * a + b;
-#pragma unroll
-            for (int i = 0; i < kSlice4; ++i) o4[i] = o4[i] * a + b * src[i];
-            rm = nm;
-        }
-#pragma unroll
-        for (int sh = 4; sh < 64; sh <<= 1) {
-            const float om = __shfl_xor(rm, sh), ow = __shfl_xor(rw, sh);
-            const float nm = fmaxf(rm, om);
-            const float a = rm == -INFINITY ? 0.f : __expf(rm - nm);
-            const float b = om == -INFINITY ? 0.f : __expf(om - nm);
-            rw = rw * a + ow * b;
-#pragma unroll
-            for (int i = 0; i < kSlice4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o4[i][e] = o4[i][e] * a + __shfl_xor(o4[i][e], sh) * b;
-            rm = nm;
-        }
-        const bool empty = rm == -INFINITY || !(rw > 0.f);
-        if (cg == 0) {
-            const float inv = empty ? 0.f : 1.0f / rw;
-            u32x4 w4[kSlice4 / 2];
-#pragma unroll
-            for (int i = 0; i < kSlice4; ++i) {
-                w4[i >> 1][(i & 1) * 2 + 0] = pack_bf16x2(o4[i][0] * inv, o4[i][1] * inv);
-                w4[i >> 1][(i & 1) * 2 + 1] = pack_bf16x2(o4[i][2] * inv, o4[i][3] * inv);
+        for (int e = 0; e < kCols; ++e) o[e] = 0.f;
+        for (int c0 = 0; c0 < nc; c0 += kBatch) {
+            const int nb = nc - c0 < kBatch ? nc - c0 : kBatch;
+            float m = -INFINITY, l = 0.f;
+            if (lane < nb) {
+                const int64_t row = (int64_t)(c0 + lane) * p.hq + h;
+                m = p.pm[row];
+                l = p.pl[row];
             }
-            u32x4* dst = reinterpret_cast<u32x4*>(p.o + (int64_t)h * kD + ds * (D / 4));
+            // chunk rows are hq * D floats apart: one uniform row pointer walks them, every
+            // load uses the same per-lane offset
+            float a[kBatch][kCols];
+            const float* rowp = p.pa + ((int64_t)c0 * p.hq + h) * kD;
+            const int64_t row_step = (int64_t)p.hq * kD;
 #pragma unroll
-            for (int i = 0; i < kSlice4 / 2; ++i) dst[i] = w4[i];
-            if (ds == 0 && p.lse) p.lse[h] = empty ? -INFINITY : rm + __logf(rw);
+            for (int jb = 0; jb < kBatch; ++jb) {
+#pragma unroll
+                for (int e = 0; e < kCols; ++e) a[jb][e] = 0.f;
+                if (jb < nb) {
+#pragma unroll
+                    for (int e = 0; e < kCols; ++e) a[jb][e] = rowp[lane * kCols + e];
+                }
+                rowp += row_step;
+            }
+            const float nM = fmaxf(M, wave_max(m));
+            const float so = M == -INFINITY ? 0.f : __expf(M - nM);
+            const float w = m == -INFINITY ? 0.f : l * __expf(m - nM);
+            W = W * so + wave_sum(w);
+#pragma unroll
+            for (int e = 0; e < kCols; ++e) o[e] *= so;
+#pragma unroll
+            for (int jb = 0; jb < kBatch; ++jb) {
+                if (jb < nb) {
+                    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), jb));
+#pragma unroll
+                    for (int e = 0; e < kCols; ++e) o[e] = fmaf(wj, a[jb][e], o[e]);
+                }
+            }
+            M = nM;
         }
+        const bool empty = M == -INFINITY || !(W > 0.f);
+        const float inv = empty ? 0.f : 1.0f / W;
+        if constexpr (kCols == 2)
+            *reinterpret_cast<uint32_t*>(p.o + (int64_t)h * kD + lane * 2) = pack_bf16x2(o[0] * inv, o[1] * inv);
+        else
+            p.o[(int64_t)h * kD + lane] = to_bf16(o[0] * inv);
+        if (lane == 0 && p.lse) p.lse[h] = empty ? -INFINITY : M + __logf(W);
     }
     // ready for the next call on this stream
     if (tid == 0) __hip_atomic_store(&p.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
