@@ -136,12 +136,71 @@ def test_decode_kv8_equals_bf16_decode_on_representable_values():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.timeout(400)
-def test_decode_kv8_full_8b_32k():
-    """The 8b_32k workload (Hq=32, Hkv=8, d=128, L=32768, 4 shards) at full size: the GPU's
-    scales and codes of the whole context equal the oracle's, and the first and last of T
-    decode steps over the oracle-made E4M3 cache match the oracle."""
-    cfg = CONFIGS["8b_32k"]
+def test_quantize_and_kv8_decode_replayed_from_a_hip_graph():
+    """The scales, the quantisation of K and V and T E4M3 decode steps, captured in one HIP
+    graph (the library allocates nothing and records no memsets), replay bit-identically to
+    the eager calls, with eager work between the replays."""
+    cfg = _cfg(8, 2, 3000, 3000, lq=16, T=3, S=3, seed=89)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    bounds = [0, 1000, 2000, 3000]
+    T, lq, cap, d = cfg.decode_steps, cfg.lq, cfg.tail_cap, cfg.d
+
+    def buffers():
+        kt = torch.zeros((cfg.hkv, cap, d), dtype=torch.bfloat16, device=DEV)
+        vt = torch.zeros_like(kt)
+        kt[:, :lq] = p2["k_qry"]
+        vt[:, :lq] = p2["v_qry"]
+        return dict(ks=torch.empty(cfg.hkv, dtype=torch.float32, device=DEV),
+                    vs=torch.empty(cfg.hkv, dtype=torch.float32, device=DEV),
+                    k8=torch.empty(k.shape, dtype=torch.uint8, device=DEV),
+                    v8=torch.empty(v.shape, dtype=torch.uint8, device=DEV), kt=kt, vt=vt,
+                    ws=sa.decode_workspace(cfg.L, cap, 3, cfg.hq, cfg.hkv, d, DEV),
+                    o=[torch.empty((cfg.hq, d), dtype=torch.bfloat16, device=DEV) for _ in range(T)],
+                    l=[torch.empty((cfg.hq,), dtype=torch.float32, device=DEV) for _ in range(T)])
+
+    def run(b):
+        sa.star_kv_fp8_scales(k, b["ks"])
+        sa.star_kv_quantize_fp8(k, b["ks"], b["k8"])
+        sa.star_kv_fp8_scales(v, b["vs"])
+        sa.star_kv_quantize_fp8(v, b["vs"], b["v8"])
+        for t in range(T):
+            sa.star_decode_step_kv8(p2["q_dec"][t], p2["k_dec"][t], p2["v_dec"][t], b["k8"], b["v8"], b["ks"], b["vs"],
+                                    bounds, b["kt"], b["vt"], lq + t, o=b["o"][t], lse=b["l"][t], workspace=b["ws"])
+
+    eager = buffers()
+    run(eager)
+    g = buffers()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in ("ks", "vs", "k8", "v8", "kt", "vt"):
+            assert torch.equal(g[name], eager[name]), "replay %d: %s differs" % (rep, name)
+        for t in range(T):
+            assert torch.equal(g["o"][t], eager["o"][t]), "replay %d step %d: O differs" % (rep, t)
+            assert torch.equal(g["l"][t], eager["l"][t]), "replay %d step %d: LSE differs" % (rep, t)
+        # unrelated eager work between replays, and outputs cleared
+        sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor)
+        for name in ("ks", "vs", "k8", "v8"):
+            g[name].zero_()
+        for t in range(T):
+            g["o"][t].zero_()
+            g["l"][t].zero_()
+        torch.cuda.synchronize()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["8b_32k", "8b_128k_needle"])
+def test_decode_kv8_full(name):
+    """A workload at full size (8b_32k: Hq=32, Hkv=8, d=128, L=32768, 4 shards; 8b_128k_needle:
+    L=131072 with a planted needle key per kv head): the GPU's scales and codes of the whole
+    context equal the oracle's, and the first and last of T decode steps over the oracle-made
+    E4M3 cache match the oracle."""
+    cfg = CONFIGS[name]
     flush_print("kv8 full", cfg.name)
     x = sin.all_inputs(cfg, DEV)
     k, v = x["k_ctx"], x["v_ctx"]
@@ -172,6 +231,6 @@ def test_decode_kv8_full_8b_32k():
     kt, vt = k_tail.cpu(), v_tail.cpu()
     for t in (0, T - 1):
         ro, rl = of8.phase2_decode_kv8(x["q_dec"][t].cpu(), hk8, hv8, hks, hvs, bounds, kt, vt, cfg.lq + t + 1)
-        assert_out(od[t], ro, "8b_32k kv8 decode step %d O" % t)
-        assert_lse(ld[t], rl, "8b_32k kv8 decode step %d LSE" % t)
+        assert_out(od[t], ro, "%s kv8 decode step %d O" % (name, t))
+        assert_lse(ld[t], rl, "%s kv8 decode step %d LSE" % (name, t))
     flush_print("  kv8 decode ok")
