@@ -22,14 +22,14 @@
 // B-operand layout of the second product O^T += V^T P^T, whose V^T operand is
 // read from the row-major V tile with transposing LDS reads.
 //
-// Tiles of 64 keys are double-buffered in LDS and copied there by direct
+// Tiles of 64 keys go through a ring of four LDS stages, copied there by direct
 // global-to-LDS loads, which take no registers and no LDS store instructions;
-// the copy of tile j+1 is in flight while tile j is multiplied.  The two stages
-// are separate LDS objects so that reads of one never wait for the copy into
-// the other.  Softmax runs in the exp2 domain with a lazily updated reference
-// max: the accumulators are only rescaled when a row's max grows by more than
-// 2^8, which keeps every probability below 256 and is exact after the final
-// normalisation.
+// the copy of tile j+3 is in flight while tile j is multiplied.  Each tile runs
+// as two 32-key halves so that one half's exponentials issue between the other
+// half's MFMAs.  Softmax runs in the exp2 domain with a lazily updated
+// reference max: the accumulators are only rescaled when a row's max grows by
+// more than 2^8, which keeps every probability below 256 and is exact after
+// the final normalisation.
 #include "common.h"
 #include "internal.h"
 
@@ -78,7 +78,20 @@ __device__ __forceinline__ u32x2v lds_read_tr(const char* p) {
     return __builtin_bit_cast(u32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+// One 16-byte-per-lane global-to-LDS copy (global_load_lds_dwordx4), issued from asm so that
+// the compiler's wait insertion does not track it: with the builtin it cannot tell the LDS
+// stages apart and waits for every copy in flight before each barrier.  Copies are waited
+// for explicitly (s_waitcnt vmcnt before the barrier that publishes a stage).  LDS reads
+// still complete in order among themselves, so the compiler's partial lgkmcnt waits stay
+// correct.  The s_nop is the wait state an M0 write needs before a load that writes LDS.
+// gbase and lds_addr are wave-uniform; voff is this lane's byte offset.
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 : : "v"(voff), "s"(gbase), "s"(lds_addr) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
 
 // Copy one K/V tile straight from global memory into an LDS stage (no registers).
 // One instruction fills one 1 KB block (lane i writes bytes 16i .. 16i+15 of it):
@@ -102,8 +115,17 @@ __device__ __forceinline__ void dma_tile(char* stage, const uint16_t* __restrict
         const int row = b + T::kBlocks * (lane / T::kChunks);
         const int key = min(key0 + row, kmax - 1);
         const uint32_t off = (uint32_t)key * T::kRowBytes + (uint32_t)(lane % T::kChunks) * 16u;
-        __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_void*)(dst + b * blk_bytes), 16, 0, 0);
+        lds_copy16(src, off, lds_addr_of(dst + b * blk_bytes));
     }
+}
+
+// s_waitcnt operand that waits until at most two tile copies (this wave's share of each:
+// Geo<D>::kBlocks / 4 loads) are outstanding; expcnt and lgkmcnt at their "no wait" maxima.
+template <int D>
+constexpr int wait_two_copies() {
+    constexpr int n = 2 * (Geo<D>::kBlocks / 4);
+    static_assert(n < 64, "vmcnt field");
+    return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
 }
 
 // Description of the keys one workgroup visits: segment A (tiles [0, nta)),
@@ -127,6 +149,8 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     constexpr int kD = D;
     __shared__ __attribute__((aligned(16))) char smem0[T::kStageBytes];
     __shared__ __attribute__((aligned(16))) char smem1[T::kStageBytes];
+    __shared__ __attribute__((aligned(16))) char smem2[T::kStageBytes];
+    __shared__ __attribute__((aligned(16))) char smem3[T::kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -248,67 +272,86 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
 
     f32x16 s[kKB];   // S^T of the current tile, one 32-key block per entry
 
-    // Mask tile j's scores in place where the tile can hold an invisible key.
-    auto mask = [&](int j) {
-        const int key0 = tile_key0(j);
-        const bool in_a = j < kp.nta;
-        const int seg_hi = in_a ? (int)kp.a_hi : (int)kp.b_hi;
-        bool need = key0 + kBN > seg_hi;
-        if (!in_a && kp.causal) need |= (int64_t)key0 + kBN - 1 > row0 + kp.diag;
-        if (need) {
-            const int lim = min(seg_hi - key0, kBN);
-            const int64_t r64 = (in_a || !kp.causal) ? (int64_t)kBN : qrow + kp.diag - key0;
-            const int rlim = r64 > kBN ? kBN : (r64 < -1 ? -1 : (int)r64);
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rel = kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-                    if (rel >= lim || rel > rlim) s[kb][r] = -INFINITY;
-                }
-        }
-    };
-
     // transposing-read addressing inside a 16-key step (see the P.V comment below)
     const int trow = 4 * half + ((lane & 15) >> 2);
     const int tcol = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    // One 64-key tile as two 32-key halves: half 0's exponentials issue between half 1's
+    // score MFMAs, and half 1's between half 0's P.V MFMAs, so that no stretch of the
+    // softmax runs without MFMAs of the same wave in flight.
     auto step = [&](int j, const char* cur, char* nxt) {
-        if (j + 1 < nt) dma_tile<D>(nxt, kbase, vbase, tile_key0(j + 1), kmax, uwave, lane);
+        // Copy tile j + 3 into the stage read during step j - 1 (every wave is past it).  The
+        // last three steps copy the last tile again, into stages nobody reads, so that exactly
+        // two copies are in flight behind every wait below.
+        dma_tile<D>(nxt, kbase, vbase, tile_key0(min(j + 3, nt - 1)), kmax, uwave, lane);
+        // Masking: does tile j hold a key that some row may not see (uniform)?
+        const int key0 = tile_key0(j);
+        const bool in_a = j < kp.nta;
+        const int seg_hi = in_a ? (int)kp.a_hi : (int)kp.b_hi;
+        bool need = key0 + kBN > seg_hi;
+        if (!in_a && kp.causal) need |= (int64_t)key0 + kBN - 1 > row0 + kp.diag;
+        const int lim = min(seg_hi - key0, kBN);
+        int rlim = kBN;
+        if (!in_a && kp.causal) {
+            const int64_t r64 = qrow + kp.diag - key0;
+            rlim = r64 > kBN ? kBN : (r64 < -1 ? -1 : (int)r64);
+        }
+        // Phase-2 partials take every tile's max (they report the true max); Phase 1 takes it
+        // on its first tile only and otherwise checks the sum bound after the exponentials.
+        const bool take_max = MODE == 1 || j == 0;
+
         const char* vs = cur + T::kKTileBytes;
         // K operand: row kb*32 + col, chunk 2*st + half: row col is in block col % NB at
         // position col / NB; kb adds 32 rows, i.e. 32/NB positions of 2D bytes (512 B).
-        const char* kp = cur + (col % T::kBlocks) * kKBlock + (col / T::kBlocks) * T::kRowBytes + half * 16;
+        const char* kop = cur + (col % T::kBlocks) * kKBlock + (col / T::kBlocks) * T::kRowBytes + half * 16;
         // V operand rows 16u + trow (+8): block trow (+8), row u inside it.
         const char* vp = vs + trow * kVBlock + tcol * 2;   // trow < 8 <= NB: block trow, position 0
 
-        // ---- S^T = K Q^T, one 32-key block at a time, all eight K operands read first
-        auto scores = [&]() {
+        auto read_k = [&](int kb, u32x4 (&ka)[T::kST]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb) {
-                u32x4 ka[T::kST];
+            for (int st = 0; st < T::kST; ++st) ka[st] = *reinterpret_cast<const u32x4*>(kop + kb * 512 + st * 32);
+        };
+        // V^T operands of 16-key steps 2kb and 2kb+1 by transposing reads of the row-major V
+        // tile.  Step u: slot i of lane half h is key 16u + 8*(i/4) + 4h + i%4, the S^T
+        // layout.  In a 16-lane group, source lane s points at key (s/4) of a four-key set
+        // and at columns 4*(s%4) .. +3 of the group's 16-wide head-dim slice; result lane i
+        // holds column i of that slice for the four keys.
+        auto read_v = [&](int kb, u32x4 (&va)[2][T::kDB]) __attribute__((always_inline)) {
 #pragma unroll
-                for (int st = 0; st < T::kST; ++st)
-                    ka[st] = *reinterpret_cast<const u32x4*>(kp + kb * 512 + st * 32);
+            for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+                for (int db = 0; db < T::kDB; ++db) {
+                    // row 16u + trow: 16 rows are 16/NB positions of 2D bytes (256 B) further on
+                    const int u = 2 * kb + uu;
+                    const u32x2v a0 = lds_read_tr(vp + u * 256 + db * 64);
+                    const u32x2v a1 = lds_read_tr(vp + T::kPlus8 + u * 256 + db * 64);
+                    va[uu][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                }
+        };
+        auto score_mfma = [&](int kb, int st, const u32x4 (&ka)[T::kST]) __attribute__((always_inline)) {
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s[kb], 0, 0, 0);
+        };
+        auto score_blk = [&](int kb) __attribute__((always_inline)) {
+            u32x4 ka[T::kST];
+            read_k(kb, ka);
 #pragma unroll
-                for (int st = 0; st < T::kST; ++st)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[st]), qb[st], s[kb],
-                                                                   0, 0, 0);
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+            for (int st = 0; st < T::kST; ++st) score_mfma(kb, st, ka);
+        };
+        auto mask_blk = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rel = kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                if (rel >= lim || rel > rlim) s[kb][r] = -INFINITY;
             }
         };
-        scores();
-        mask(j);
-
-        // ---- tile max; move the reference (and rescale) only if it grew past 2^8
-        auto rescale_to_max = [&]() {
-            float mx = s[0][0];
+        // Move the reference (and rescale) if this half's max grew past it by 2^8.
+        auto max_blk = [&](int kb) __attribute__((always_inline)) {
+            float mx = s[kb][0];
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             mx = half_pair_max(mx) * sl2;
             mtrue = fmaxf(mtrue, mx);
             if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleThreshold)) {
@@ -320,85 +363,150 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
                 for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                // Half 0's probabilities are taken before half 1's max and enter the
+                // accumulators only afterwards: they move to the new reference too (once
+                // they are in the accumulators this is a harmless write to dead values).
+                if (kb == 1) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[0][r] *= alpha;
+                }
             }
         };
-        // Phase-2 partials report the true max, so they take the max of every tile; Phase 1
-        // takes it on its first tile only (see below).
-        if (MODE == 1 || j == 0) rescale_to_max();
-
-        // ---- P^T = exp2(S^T - ref) in place, row sums from the unrounded values
-        auto exps = [&]() -> float {
-            const float negm = -mref;
-            float ls = 0.f;
+        auto exp_one = [&](int kb, int r, float negm, float& ls) __attribute__((always_inline)) {
+            s[kb][r] = fast_exp2(fmaf(s[kb][r], sl2, negm));
+            ls += s[kb][r];
+        };
+        // Phase 1 keeps a half when every row's sum of its probabilities is at most 2^20: no
+        // probability overflowed and the accumulators stay far from the fp32 range, so the
+        // reference need not move.  Else (scores far above the reference) the half's scores
+        // are recomputed from the K tile, the reference moves to their max and the
+        // probabilities are redone.  This replaces a max over every tile's scores.
+        auto check = [&](int kb, float ls) __attribute__((always_inline)) -> float {
+            if (MODE == 0 && __builtin_amdgcn_ballot_w64(!(ls <= kSumBound))) {
+                score_blk(kb);
+                if (need) mask_blk(kb);
+                max_blk(kb);
+                const float negm = -mref;
+                ls = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[kb][r] = fast_exp2(fmaf(s[kb][r], sl2, negm));
-                    ls += s[kb][r];
-                }
+                for (int r = 0; r < 16; ++r) exp_one(kb, r, negm, ls);
+            }
             return ls;
         };
-        float ls = exps();
-        // Phase 1 keeps the tile when every row's sum of probabilities is at most 2^20: no
-        // probability overflowed and the accumulators stay far from the fp32 range, so the
-        // reference need not move.  Else (scores far above the reference) the scores are
-        // recomputed from the K tile, the reference moves to their max and the probabilities
-        // are redone.  This replaces a max over every tile's scores.
-        if (MODE == 0 && __builtin_amdgcn_ballot_w64(!(ls <= kSumBound))) {
-            scores();
-            mask(j);
-            rescale_to_max();
-            ls = exps();
-        }
-        lsum += ls;
-
-        // ---- V^T operands by transposing reads of the row-major V tile.  16-key step u:
-        //      slot i of lane half h is key 16u + 8*(i/4) + 4h + i%4, the S^T layout.  In a
-        //      16-lane group, source lane s points at key (s/4) of a four-key set and at
-        //      columns 4*(s%4) .. +3 of the group's 16-wide head-dim slice; result lane i
-        //      holds column i of that slice for the four keys.
-        u32x4 va[2 * kKB][T::kDB];
-#pragma unroll
-        for (int u = 0; u < 2 * kKB; ++u)
-#pragma unroll
-            for (int db = 0; db < T::kDB; ++db) {
-                // row 16u + trow: 16 rows are 16/NB positions of 2D bytes (256 B) further on
-                const u32x2v a0 = lds_read_tr(vp + u * 256 + db * 64);
-                const u32x2v a1 = lds_read_tr(vp + T::kPlus8 + u * 256 + db * 64);
-                va[u][db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-            }
-
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int u = 0; u < 2 * kKB; ++u) {
+        auto pack = [&](int kb, int uu) __attribute__((always_inline)) -> bf16x8 {
             u32x4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                w[i] = pack_bf16x2(s[u >> 1][8 * (u & 1) + 2 * i], s[u >> 1][8 * (u & 1) + 2 * i + 1]);
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
+            for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(s[kb][8 * uu + 2 * i], s[kb][8 * uu + 2 * i + 1]);
+            return __builtin_bit_cast(bf16x8, w);
+        };
+        constexpr int kEPM = 16 / T::kST;         // half-0 exponentials per half-1 score MFMA
+        constexpr int kEPV = 16 / (2 * T::kDB);   // half-1 exponentials per half-0 P.V MFMA
+
+        // ---- half 0 scores; half 1's K operands read while they run
+        u32x4 ka[T::kST];
+        {
+            u32x4 k0[T::kST];
+            read_k(0, k0);
 #pragma unroll
-            for (int db = 0; db < T::kDB; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[u][db]), pb,
-                                                                 acc[db], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) s[0][r] = 0.f;
+#pragma unroll
+            for (int st = 0; st < T::kST; ++st) score_mfma(0, st, k0);
+            read_k(1, ka);
+            __builtin_amdgcn_sched_group_barrier(0x100, T::kST, 0);
+#pragma unroll
+            for (int st = 0; st < T::kST; ++st) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
-        // This wave's copies into `nxt` have landed; after the barrier every wave's have,
-        // and every wave is done reading `cur`.
-        __builtin_amdgcn_s_waitcnt(0);
+        if (need) mask_blk(0);
+        if (take_max) max_blk(0);
+        // ---- half 1 scores || half 0 exponentials and V operands
+        float ls0 = 0.f;
+        u32x4 va[2][T::kDB];
+        {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[1][r] = 0.f;
+            const float negm = -mref;
+#pragma unroll
+            for (int st = 0; st < T::kST; ++st) {
+                score_mfma(1, st, ka);
+#pragma unroll
+                for (int e = 0; e < kEPM; ++e) exp_one(0, st * kEPM + e, negm, ls0);
+            }
+            read_v(0, va);
+#pragma unroll
+            for (int st = 0; st < T::kST; ++st) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * T::kDB / T::kST, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3 * kEPM, 0);
+            }
+        }
+        lsum += check(0, ls0);
+        if (need) mask_blk(1);
+        if (take_max) max_blk(1);
+        // ---- half 0 P.V || half 1 exponentials and V operands
+        float ls1 = 0.f;
+        u32x4 vb[2][T::kDB];
+        {
+            const bf16x8 p0 = pack(0, 0), p1 = pack(0, 1);
+            const float negm = -mref;
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db) {
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[uu][db]),
+                                                                     uu ? p1 : p0, acc[db], 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < kEPV; ++e) exp_one(1, (uu * T::kDB + db) * kEPV + e, negm, ls1);
+                }
+            read_v(1, vb);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+            for (int m = 0; m < 2 * T::kDB; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3 * kEPV, 0);
+            }
+        }
+        lsum += check(1, ls1);
+        // ---- half 1 P.V
+        {
+            const bf16x8 p0 = pack(1, 0), p1 = pack(1, 1);
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+                for (int db = 0; db < T::kDB; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vb[uu][db]),
+                                                                     uu ? p1 : p0, acc[db], 0, 0, 0);
+        }
+        // This wave's copies of tile j + 1 have landed (those of tiles j + 2 and j + 3 may still
+        // be in flight); after the barrier every wave's have, and every wave is done reading
+        // `cur`.
+        __builtin_amdgcn_s_waitcnt(wait_two_copies<D>());
         __syncthreads();
     };
 
     if (nt > 0) {
-        dma_tile<D>(smem0, kbase, vbase, tile_key0(0), kmax, uwave, lane);
+        // The query loads have landed: from here on the only loads in flight are tile copies,
+        // which the waits count.  Tiles 0-2 go into stages 0-2; tile j lives in stage j % 4.
         __builtin_amdgcn_s_waitcnt(0);
+        dma_tile<D>(smem0, kbase, vbase, tile_key0(0), kmax, uwave, lane);
+        dma_tile<D>(smem1, kbase, vbase, tile_key0(min(1, nt - 1)), kmax, uwave, lane);
+        dma_tile<D>(smem2, kbase, vbase, tile_key0(min(2, nt - 1)), kmax, uwave, lane);
+        __builtin_amdgcn_s_waitcnt(wait_two_copies<D>());
         __syncthreads();
         int j = 0;
-        for (; j + 1 < nt; j += 2) {
-            step(j, smem0, smem1);
+        for (; j + 3 < nt; j += 4) {
+            step(j, smem0, smem3);
             step(j + 1, smem1, smem0);
+            step(j + 2, smem2, smem1);
+            step(j + 3, smem3, smem2);
         }
-        if (j < nt) step(j, smem0, smem1);
+        if (j < nt) step(j, smem0, smem3);
+        if (j + 1 < nt) step(j + 1, smem1, smem0);
+        if (j + 2 < nt) step(j + 2, smem2, smem1);
+        __builtin_amdgcn_s_waitcnt(0);   // the trailing copies
     }
 
     // ---------------------------------------------------------------- epilogue

@@ -132,6 +132,41 @@ def test_phase1_scores_jumping_past_the_reference():
     assert_lse(lse, rl, "LSE")
 
 
+def test_score_jump_in_the_second_half_of_a_tile():
+    """A score far above every earlier one among keys 32..63 of a 64-key tile: the kernels
+    take a tile's first half of probabilities before its second half's max, so when that max
+    moves the reference the pending probabilities must move with it.  Phase 1 meets this on a
+    work item's first tile (the anchor tile), Phase-2 partials on any tile."""
+    hq, hkv, L, b, a = 8, 2, 1000, 320, 320
+    G = hq // hkv
+    cfg = _cfg(hq, hkv, L, b, a, seed=53)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    k = k.clone()
+    for g in range(hkv):                       # row 400 (block 1) meets anchor key 40
+        k[g, 40] = (8 * q[g * G, 400].float()).to(k.dtype)
+    o, lse = sa.star_phase1_encode(q, k, v, b, a)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase1(q.cpu(), k.cpu(), v.cpu(), b, a)
+    assert rl[0, 400] > 40.0
+    assert_out(o, ro, "phase-1 O")
+    assert_lse(lse, rl, "phase-1 LSE")
+
+    rows, n = 20, 1000
+    qq = sin.randn(cfg, "q_qry", (hq, rows, 128), DEV)
+    kk = sin.randn(cfg, "k_ctx", (hkv, n, 128), DEV).clone()
+    vv = sin.randn(cfg, "v_ctx", (hkv, n, 128), DEV)
+    for g in range(hkv):                       # tile 0 and tile 5, both in the second half
+        kk[g, 40] = (8 * qq[g * G, 3].float()).to(kk.dtype)
+        kk[g, 5 * 64 + 50] = (10 * qq[g * G + 1, 7].float()).to(kk.dtype)
+    am, mm, lm = sa.star_phase2_partial(qq, kk, vv, n * 128, n, -1)
+    torch.cuda.synchronize()
+    ra, rm, rl2 = oracle.partial(qq.cpu(), kk.cpu(), vv.cpu(), 0, n, -1)
+    assert float(np.max(rm)) > 40.0
+    assert_out(am, ra, "partial A")
+    assert_lse(mm + torch.log(lm), rm + np.log(rl2), "partial LSE")
+    assert_lse(mm, rm, "m (largest scaled score)")
+
+
 def test_phase1_locality_bitwise():
     """Keys outside a row's visible set cannot change its output, bit for bit."""
     cfg = _cfg(8, 2, 768, 256, 256)
