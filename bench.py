@@ -64,8 +64,8 @@ def read_traffic(launch_flops_unit_bytes=None):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="8b_32k")
     ap.add_argument("--block", type=int, default=None, help="override the workload's block size")
     ap.add_argument("--anchor", type=int, default=None, help="override the workload's anchor size")
