@@ -20,9 +20,11 @@
 // O^T += V^T P^T takes V^T from a wave-private LDS copy of the V tile (stored
 // row-major, read back with the transposing ds_read_b64_tr_b16).  Each wave
 // keeps an online softmax; the four waves are combined in LDS into one partial
-// (A, m, l) per chunk.  The last workgroup of a kv head to finish (an atomic
-// ticket in the workspace) merges that head's chunk partials in log space and
-// writes the output, then resets its ticket counter to zero.
+// (A, m, l) per chunk.  With up to four q heads per kv head, the last workgroup
+// of a kv head to finish (an atomic ticket in the workspace) merges that head's
+// chunk partials in log space and writes the output, then resets its ticket
+// counter to zero.  With more q heads the launcher runs merge_kernel over the
+// same partials instead.
 //
 // The KV8 instantiations read the context hosts' partitions as E4M3 codes with
 // one scale per kv head for K and for V (kvfp8.hip).  The codes are widened to
@@ -65,6 +67,7 @@ struct DecodeArgs {
     unsigned* tickets;  // [hkv], zero between calls
     uint16_t* o;        // [hq][d]
     float* lse;         // [hq] or null
+    int merge_here;     // the last chunk of a kv head merges (else merge_kernel runs next)
 };
 
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
@@ -394,6 +397,7 @@ decode_kernel(const DecodeArgs p) {
         }
     }
 
+    if (!p.merge_here) return;
     // ---- the last chunk of this kv head to finish merges all of them.
     // The partial was written with device-scope stores, so once they have completed
     // (vmcnt 0) every workgroup can see it.  A device-scope release fence would add a
@@ -541,9 +545,15 @@ hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, cons
     const bool kv8 = k8 != nullptr;
     if (kv8 && (!v8 || !k_scale || !v_scale)) return hipErrorInvalidValue;
     const dim3 gd((unsigned)grid);
-    if (d == 128) return kv8 ? launch_decode_g<128, true>(a, gd, stream) : launch_decode_g<128, false>(a, gd, stream);
-    if (d == 64) return kv8 ? launch_decode_g<64, true>(a, gd, stream) : launch_decode_g<64, false>(a, gd, stream);
-    return hipErrorInvalidValue;
+    // Up to four q heads per kv head, the last chunk of each kv head merges in the same launch
+    // (one wave per q head).  With more, a wave would merge several q heads one after the
+    // other; merge_kernel over the same partials (one workgroup per q head) is then faster.
+    a.merge_here = a.G <= kWaves;
+    hipError_t e = hipErrorInvalidValue;
+    if (d == 128) e = kv8 ? launch_decode_g<128, true>(a, gd, stream) : launch_decode_g<128, false>(a, gd, stream);
+    if (d == 64) e = kv8 ? launch_decode_g<64, true>(a, gd, stream) : launch_decode_g<64, false>(a, gd, stream);
+    if (e != hipSuccess || a.merge_here) return e;
+    return launch_merge(part_a, part_m, part_l, plan.n_chunks, hq, d, o, true, lse, nullptr, nullptr, stream);
 }
 
 }  // namespace star

@@ -207,9 +207,10 @@ star_status_t star_softmax_merge(const float *a, const float *m, const float *l,
  *         counters back at zero).  Calls that share a workspace must be
  *         ordered on one stream.
  *   0 <= tail_len < tail_cap.
- * bf16 with d = 64 or 128: one kernel launch (chunk partials, the append, and the
- * merge done by the last chunk of each kv head).  Other shapes: an append
- * launch and a vector-path launch.
+ * bf16 with d = 64 or 128 and hq/hkv <= 4: one kernel launch (chunk partials,
+ * the append, and the merge done by the last chunk of each kv head); hq/hkv of
+ * 8 or 16: that launch without the merge, then a merge launch.  Other shapes:
+ * an append launch and a vector-path launch.
  */
 size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards,
                                    int32_t hq, int32_t hkv, int32_t d);
@@ -268,7 +269,7 @@ star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32_t hkv, i
  *   dt must be STAR_BF16 (q_new, k_new, v_new, the query-host cache and o),
  *   d 64 or 128 and hq/hkv one of 1, 2, 4, 8, 16; other shapes return
  *   STAR_ERR_UNSUPPORTED.  The workspace is star_decode_workspace_bytes(...)
- *   bytes, with the same rules.  One kernel launch.
+ *   bytes, with the same rules.  Launches as star_decode_step's bf16 path.
  */
 star_status_t star_decode_step_kv8(const void *q_new, const void *k_new, const void *v_new,
                                    const void *k_ctx8, const void *v_ctx8,

@@ -421,10 +421,11 @@ def test_batch_as_folded_heads(d):
         assert_lse(ld[qs], rl, "decode LSE, sequence %d" % i)
 
 
-def test_decode_steps_replayed_from_a_hip_graph():
+@pytest.mark.parametrize("hq", [8, 16])   # G = 4: merge in the decode launch; G = 8: merge_kernel after it
+def test_decode_steps_replayed_from_a_hip_graph(hq):
     """T decode steps captured in one HIP graph (the library allocates nothing and records no
     memsets) replay bit-identically to the eager calls, with eager work between replays."""
-    cfg = _cfg(8, 2, 3000, 1000, 1000, lq=16, T=4, S=3, seed=43)
+    cfg = _cfg(hq, 2, 3000, 1000, 1000, lq=16, T=4, S=3, seed=43)
     q, k, v = sin.phase1_inputs(cfg, DEV)
     p2 = sin.phase2_inputs(cfg, DEV)
     bounds = shard_bounds(cfg.L, cfg.block, cfg.shards)
