@@ -421,6 +421,42 @@ def test_batch_as_folded_heads(d):
         assert_lse(ld[qs], rl, "decode LSE, sequence %d" % i)
 
 
+def test_phase1_and_query_replayed_from_a_hip_graph():
+    """Phase 1 and the query phase captured in one HIP graph replay bit-identically to the eager
+    calls (several replays, eager work and synchronisation between them)."""
+    cfg = _cfg(8, 2, 2600, 1000, 1000, lq=40, T=1, S=3, seed=59)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    bounds = shard_bounds(cfg.L, cfg.block, cfg.shards)
+    kt = torch.zeros((cfg.hkv, cfg.tail_cap, cfg.d), dtype=torch.bfloat16, device=DEV)
+    vt = torch.zeros_like(kt)
+    kt[:, :cfg.lq] = p2["k_qry"]
+    vt[:, :cfg.lq] = p2["v_qry"]
+    o_e, l_e = sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor)
+    oq_e, lq_e = sa.star_phase2_query(p2["q_qry"], k, v, bounds, kt, vt, cfg.lq)
+    torch.cuda.synchronize()
+    o = torch.empty_like(o_e)
+    lse = torch.empty_like(l_e)
+    oq = torch.empty_like(oq_e)
+    lq = torch.empty_like(lq_e)
+    ws = torch.empty(max(16, sa.star_phase2_query_workspace_bytes(cfg.lq, len(bounds) - 1, cfg.hq, cfg.hkv, cfg.d)),
+                     dtype=torch.uint8, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor, o=o, lse=lse)
+        sa.star_phase2_query(p2["q_qry"], k, v, bounds, kt, vt, cfg.lq, o=oq, lse=lq, workspace=ws)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e) and torch.equal(lse, l_e), "replay %d: Phase 1 differs" % rep
+        assert torch.equal(oq, oq_e) and torch.equal(lq, lq_e), "replay %d: query phase differs" % rep
+        for t in (o, lse, oq, lq):
+            t.zero_()
+        sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds, kt.clone(), vt.clone(),
+                            cfg.lq)
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("hq", [8, 16])   # G = 4: merge in the decode launch; G = 8: merge_kernel after it
 def test_decode_steps_replayed_from_a_hip_graph(hq):
     """T decode steps captured in one HIP graph (the library allocates nothing and records no
