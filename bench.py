@@ -14,7 +14,8 @@ launch stream, against the bf16 dense MFMA peak.  `decode` reports the decode st
 K/V stream rate (warm: inside the step; cold: after overwriting 1 GiB and reading it back,
 so the 256 MB last-level cache holds no K/V and no dirty lines).  `decode_kv8` reports the
 same decode steps over an E4M3 context cache (quantised once, after the step; its time is
-reported too) against the same bytes model with 1-byte context elements.  `cpu_baseline`
+reported too) against the same bytes model with 1-byte context elements, and the query
+phase over that cache (star_phase2_query_kv8).  `cpu_baseline`
 times the fp64 oracle on a bounded sample of Phase-1 rows on the host's cores.
 """
 from __future__ import annotations
@@ -228,6 +229,10 @@ def main():
             sa.star_decode_step_kv8(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], k8, v8, ks, vs, bounds, k_tail,
                                     v_tail, cfg.lq + t, o=od[t], lse=ld[t], workspace=ws_dec, stream=stream)
 
+        def query8():
+            sa.star_phase2_query_kv8(x["q_qry"], k8, v8, ks, vs, bounds, k_tail, v_tail, cfg.lq, o=oq, lse=lq_lse,
+                                     workspace=ws_q, stream=stream)
+
         quantize()
         qz = []
         for _ in range(3):
@@ -237,8 +242,16 @@ def main():
             b.record(stream)
             qz.append((a, b))
         for _ in range(args.warmup):
+            query8()
             for t in range(cfg.decode_steps):
                 decode8(t)
+        qreps = []
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            query8()
+            b.record(stream)
+            qreps.append((a, b))
         reps = []
         for _ in range(args.steps):
             a, b = ev(), ev()
@@ -250,6 +263,7 @@ def main():
         torch.cuda.synchronize()
         q8_ms = float(np.mean([a.elapsed_time(b) for a, b in qz]))
         d8_ms = float(np.mean([a.elapsed_time(b) for a, b in reps]))
+        qq8_ms = float(np.mean([a.elapsed_time(b) for a, b in qreps]))
         cold8 = []
         for r in range(args.cold_reps):
             flush.fill_(float(r))
@@ -269,7 +283,8 @@ def main():
                "warm_GBps": w8 / 1e9, "warm_hbm_frac": w8 / PEAK_HBM_BYTES,
                "cold_GBps": c8 / 1e9, "cold_hbm_frac": c8 / PEAK_HBM_BYTES,
                "cold_ms_per_token": float(np.mean([ms for ms, _ in cold8])),
-               "quantize_ms": q8_ms, "quantize_GBps": qbytes / (q8_ms * 1e-3) / 1e9}
+               "quantize_ms": q8_ms, "quantize_GBps": qbytes / (q8_ms * 1e-3) / 1e9,
+               "query_ms": qq8_ms, "query_tflops": cfg.phase2_query_flops() / (qq8_ms * 1e-3) / 1e12}
         del k8, v8
     del flush
 

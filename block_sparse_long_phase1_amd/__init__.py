@@ -78,6 +78,9 @@ def load_library(path: str | None = None):
         lib.star_decode_step_kv8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32,
                                              i32, ctypes.c_int, f32, vp, vp, vp, sz, vp]
         lib.star_decode_step_kv8.restype = ctypes.c_int
+        lib.star_phase2_query_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32,
+                                              i32, ctypes.c_int, f32, vp, vp, vp, sz, vp]
+        lib.star_phase2_query_kv8.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -361,10 +364,38 @@ def star_decode_step_kv8(q_new, k_new, v_new, k_ctx8, v_ctx8, k_scale, v_scale, 
     return o, lse
 
 
+def star_phase2_query_kv8(q, k_ctx8, v_ctx8, k_scale, v_scale, bounds, k_tail, v_tail, tail_len: int, o=None,
+                          lse=None, workspace=None, scale=None, want_lse: bool = True, stream=None):
+    """star_phase2_query over an E4M3 context cache: k_ctx8/v_ctx8 uint8 [Hkv,L,d] with fp32
+    scales [Hkv]; everything else bf16 as in star_phase2_query."""
+    torch = _torch()
+    hq, rows, d = q.shape
+    hkv, L, _ = k_ctx8.shape
+    tail_cap = k_tail.shape[1]
+    n_shards = len(bounds) - 1
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((hq, rows), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nb = star_phase2_query_workspace_bytes(rows, n_shards, hq, hkv, d)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    b = (ctypes.c_int64 * (n_shards + 1))(*[int(x) for x in bounds])
+    st = load_library().star_phase2_query_kv8(
+        _dev(q, "q"), rows, _u8(k_ctx8, "k_ctx8", (hkv, L, d)), _u8(v_ctx8, "v_ctx8", (hkv, L, d)),
+        _f32(k_scale, "k_scale", (hkv,)), _f32(v_scale, "v_scale", (hkv,)), L, b, n_shards,
+        _same(k_tail, q, "k_tail", (hkv, tail_cap, d)), _same(v_tail, q, "v_tail", (hkv, tail_cap, d)),
+        tail_len, tail_cap, hq, hkv, d, _dt(q), _scale(d, scale), _same(o, q, "o", (hq, rows, d)),
+        ctypes.c_void_p(0) if lse is None else _f32(lse, "lse", (hq, rows)),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "star_phase2_query_kv8")
+    return o, lse
+
+
 __all__ = [
     "CONFIGS", "StarConfig", "n_blocks", "shard_bounds", "load_library", "StarError",
     "star_phase1_encode", "star_phase2_workspace_bytes", "star_phase2_partial", "star_softmax_merge",
     "star_phase2_query_workspace_bytes", "star_phase2_query",
     "star_decode_workspace_bytes", "star_decode_step", "decode_workspace", "STAR_F32", "STAR_BF16",
-    "star_kv_fp8_scales", "star_kv_quantize_fp8", "star_decode_step_kv8",
+    "star_kv_fp8_scales", "star_kv_quantize_fp8", "star_decode_step_kv8", "star_phase2_query_kv8",
 ]

@@ -35,6 +35,16 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Eight E4M3 codes (bytes in memory order) -> eight bf16 (exact: every E4M3 value is a bf16).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    return r;
+}
+
 // Combine a value with the one held 32 lanes away (lanes l and l^32).  With the same
 // register as both operands, v_permlane32_swap returns {own, partner} in an order that
 // depends on the lane's half, so only symmetric combinations of the pair are formed.

@@ -74,16 +74,6 @@ typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
-// Eight E4M3 codes (bytes in memory order) -> eight bf16 (exact: every E4M3 value is a bf16).
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    u32x4 r;
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
-    return r;
-}
-
 // One tile's operand registers: K (the A operands of S^T) and the V pieces bound for LDS,
 // as bf16 or as E4M3 codes (half the bytes).
 template <int NK, int NV>

@@ -14,12 +14,15 @@ constexpr int kMaxParts = 65;
 struct PartPlan {
     int n_parts;
     int64_t split_len;
-    const uint16_t* k[kMaxParts];
-    const uint16_t* v[kMaxParts];
+    const void* k[kMaxParts];   // bf16 elements, or E4M3 codes for parts [0, n_f8)
+    const void* v[kMaxParts];
     int64_t head_stride[kMaxParts];
     int64_t n_kv[kMaxParts];
     int64_t causal[kMaxParts];
     int32_t split_prefix[kMaxParts + 1];
+    int n_f8;                   // parts [0, n_f8) hold E4M3 codes (with per-kv-head scales)
+    const float* k_scale;       // [hkv], for E4M3 parts
+    const float* v_scale;
 };
 
 // Arguments of the bf16 MFMA attention kernel (Phase 1 and Phase-2 partials).

@@ -141,8 +141,9 @@ struct KeyPlan {
 
 }  // namespace
 
-// MODE 0 = Phase 1 encode, 1 = Phase 2 partial; D = head dim (64 or 128).
-template <int MODE, int D>
+// MODE 0 = Phase 1 encode, 1 = Phase 2 partial; D = head dim (64 or 128).  F8 (Phase-2
+// partials only): partitions [0, plan.n_f8) hold E4M3 codes with per-kv-head scales.
+template <int MODE, int D, bool F8 = false>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_mfma_kernel(const AttnMfmaArgs p) {
     using T = Geo<D>;
@@ -176,6 +177,7 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     int64_t row0, row_end;        // query rows [row0, row_end) valid for this workgroup
     KeyPlan kp;
     int split = 0;
+    bool f8 = false;              // this work item's partition holds E4M3 codes (uniform)
     const uint16_t* kptr = p.k;   // this work item's key partition
     const uint16_t* vptr = p.v;
     int64_t hstride = p.kv_head_stride;
@@ -229,8 +231,9 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         kp.b_lo = lo;
         kp.b_hi = hi > lo ? hi : lo;
         kp.kmax = n_kv;
-        kptr = pl.k[part];
-        vptr = pl.v[part];
+        kptr = static_cast<const uint16_t*>(pl.k[part]);
+        vptr = static_cast<const uint16_t*>(pl.v[part]);
+        f8 = F8 && part < pl.n_f8;
         hstride = pl.head_stride[part];
     }
     kp.nta = (int)((kp.a_hi - kp.a_lo + kBN - 1) / kBN);
@@ -262,11 +265,51 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     float mref = kNoMax;   // reference max (log2 units) used in the exponent
     float mtrue = kNoMax;  // largest score seen (log2 units)
     float lsum = 0.f;      // this lane's half of the row sum
-    const float sl2 = p.scale_log2;
+    // score scale (log2 units); an E4M3 partition folds its kv head's K scale in
+    const float sl2 = (F8 && f8) ? p.scale_log2 * p.plan.k_scale[g] : p.scale_log2;
 
     const uint16_t* kbase = kptr + (int64_t)g * hstride;
     const uint16_t* vbase = vptr + (int64_t)g * hstride;
     const int kmax = (int)kp.kmax;
+
+    // E4M3 partitions: each thread loads D/64 16-byte pieces of a tile's codes (K pieces
+    // first, then V) three tiles ahead into registers, and widens them exactly to bf16 in the
+    // stage layout the tile copies produce, before the barrier that publishes that stage.
+    constexpr int kF8PiecesPerTensor = kBN * D / 16;          // 16-byte pieces of codes per K or V tile
+    constexpr int kF8Pieces = F8 ? 2 * kF8PiecesPerTensor / kThreads : 1;
+    u32x4 f8buf[kF8Pieces];
+    auto f8_piece = [&](int pc, int& row, int& col0, bool& is_v) __attribute__((always_inline)) {
+        const int pi = tid + pc * kThreads;
+        is_v = pi >= kF8PiecesPerTensor;
+        const int idx = is_v ? pi - kF8PiecesPerTensor : pi;
+        row = idx / (D / 16);
+        col0 = (idx % (D / 16)) * 16;
+    };
+    auto f8_load = [&](int key0) __attribute__((always_inline)) {
+        const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kptr) + (int64_t)g * hstride;
+        const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vptr) + (int64_t)g * hstride;
+#pragma unroll
+        for (int pc = 0; pc < kF8Pieces; ++pc) {
+            int row, col0;
+            bool is_v;
+            f8_piece(pc, row, col0, is_v);
+            const int key = min(key0 + row, kmax - 1);
+            f8buf[pc] = *reinterpret_cast<const u32x4*>((is_v ? vb8 : kb8) + (int64_t)key * D + col0);
+        }
+    };
+    auto f8_store = [&](char* stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int pc = 0; pc < kF8Pieces; ++pc) {
+            int row, col0;
+            bool is_v;
+            f8_piece(pc, row, col0, is_v);
+            char* dst = stage + (is_v ? T::kKTileBytes + (row % T::kBlocks) * kVBlock
+                                      : (row % T::kBlocks) * kKBlock) +
+                        (row / T::kBlocks) * T::kRowBytes + col0 * 2;
+            *reinterpret_cast<u32x4*>(dst) = e4m3x8_to_bf16x8(f8buf[pc][0], f8buf[pc][1]);
+            *reinterpret_cast<u32x4*>(dst + 16) = e4m3x8_to_bf16x8(f8buf[pc][2], f8buf[pc][3]);
+        }
+    };
     const int a_lo = (int)kp.a_lo, b_lo = (int)kp.b_lo;
     auto tile_key0 = [&](int j) -> int { return j < kp.nta ? a_lo + j * kBN : b_lo + (j - kp.nta) * kBN; };
 
@@ -284,7 +327,10 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         // Copy tile j + 3 into the stage read during step j - 1 (every wave is past it).  The
         // last three steps copy the last tile again, into stages nobody reads, so that exactly
         // two copies are in flight behind every wait below.
-        dma_tile<D>(nxt, kbase, vbase, tile_key0(min(j + 3, nt - 1)), kmax, uwave, lane);
+        if (F8 && f8)
+            f8_load(tile_key0(min(j + 3, nt - 1)));
+        else
+            dma_tile<D>(nxt, kbase, vbase, tile_key0(min(j + 3, nt - 1)), kmax, uwave, lane);
         // Masking: does tile j hold a key that some row may not see (uniform)?
         const int key0 = tile_key0(j);
         const bool in_a = j < kp.nta;
@@ -480,6 +526,7 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vb[uu][db]),
                                                                      uu ? p1 : p0, acc[db], 0, 0, 0);
         }
+        if (F8 && f8) f8_store(nxt);   // tile j + 3, into the stage every wave left at the last barrier
         // This wave's copies of tile j + 1 have landed (those of tiles j + 2 and j + 3 may still
         // be in flight); after the barrier every wave's have, and every wave is done reading
         // `cur`.
@@ -491,9 +538,18 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
         // The query loads have landed: from here on the only loads in flight are tile copies,
         // which the waits count.  Tiles 0-2 go into stages 0-2; tile j lives in stage j % 4.
         __builtin_amdgcn_s_waitcnt(0);
-        dma_tile<D>(smem0, kbase, vbase, tile_key0(0), kmax, uwave, lane);
-        dma_tile<D>(smem1, kbase, vbase, tile_key0(min(1, nt - 1)), kmax, uwave, lane);
-        dma_tile<D>(smem2, kbase, vbase, tile_key0(min(2, nt - 1)), kmax, uwave, lane);
+        if (F8 && f8) {
+            f8_load(tile_key0(0));
+            f8_store(smem0);
+            f8_load(tile_key0(min(1, nt - 1)));
+            f8_store(smem1);
+            f8_load(tile_key0(min(2, nt - 1)));
+            f8_store(smem2);
+        } else {
+            dma_tile<D>(smem0, kbase, vbase, tile_key0(0), kmax, uwave, lane);
+            dma_tile<D>(smem1, kbase, vbase, tile_key0(min(1, nt - 1)), kmax, uwave, lane);
+            dma_tile<D>(smem2, kbase, vbase, tile_key0(min(2, nt - 1)), kmax, uwave, lane);
+        }
         __builtin_amdgcn_s_waitcnt(wait_two_copies<D>());
         __syncthreads();
         int j = 0;
@@ -531,13 +587,15 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     } else {
         const int64_t out_row = (int64_t)split * p.hq * p.q_rows + hr;
         float* ap = p.a_out + out_row * kD;
+        // an E4M3 partition's values carry its kv head's V scale
+        const float inv_a = (F8 && f8) ? inv * p.plan.v_scale[g] : inv;
 #pragma unroll
         for (int db = 0; db < T::kDB; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int d0 = db * 32 + gq * 8 + half * 4;
-                const f32x4 w = {acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv,
-                                 acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv};
+                const f32x4 w = {acc[db][gq * 4 + 0] * inv_a, acc[db][gq * 4 + 1] * inv_a,
+                                 acc[db][gq * 4 + 2] * inv_a, acc[db][gq * 4 + 3] * inv_a};
                 *reinterpret_cast<f32x4*>(ap + d0) = w;
             }
         if (half == 0) {
@@ -637,9 +695,17 @@ hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv,
     a.plan = plan;
     const int64_t grid = (int64_t)hkv * n_row_tiles * plan.split_prefix[plan.n_parts];
     if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (d == 128) hipLaunchKernelGGL((attn_mfma_kernel<1, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    else if (d == 64) hipLaunchKernelGGL((attn_mfma_kernel<1, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    else return hipErrorInvalidValue;
+    const bool f8 = plan.n_f8 > 0;
+    if (f8 && (!plan.k_scale || !plan.v_scale)) return hipErrorInvalidValue;
+    if (d == 128) {
+        if (f8) hipLaunchKernelGGL((attn_mfma_kernel<1, 128, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_mfma_kernel<1, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    } else if (d == 64) {
+        if (f8) hipLaunchKernelGGL((attn_mfma_kernel<1, 64, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((attn_mfma_kernel<1, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

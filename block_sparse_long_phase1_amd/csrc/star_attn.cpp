@@ -87,6 +87,76 @@ star_status_t check_decode(const void* q_new, const void* k_new, const void* v_n
     return STAR_OK;
 }
 
+// Checks shared by both query-phase entry points (the context pointers are checked by each).
+star_status_t check_query(const void* q, int32_t rows, int64_t L, const int64_t* shard_bounds, int32_t n_shards,
+                          const void* k_tail, const void* v_tail, int64_t tail_len, int64_t tail_cap, int32_t hq,
+                          int32_t hkv, int32_t d, star_dtype_t dt, float scale, const void* o, const float* lse) {
+    if (!q || !k_tail || !v_tail || !o || !shard_bounds) return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+    if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
+    if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
+    if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
+    if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
+        return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
+    for (int r = 0; r < n_shards; ++r)
+        if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
+    if (tail_len < rows || tail_len > tail_cap)
+        return fail(STAR_ERR_INVALID_ARG, "need rows <= tail_len <= tail_cap (rows %d, tail_len %lld, tail_cap %lld)",
+                    rows, (long long)tail_len, (long long)tail_cap);
+    if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+    star_status_t s = check_heads(hq, hkv, d, dt);
+    if (s != STAR_OK) return s;
+    if (!aligned16(q) || !aligned16(k_tail) || !aligned16(v_tail) || !aligned16(o) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    return STAR_OK;
+}
+
+// The query phase on the MFMA kernel: one partial launch over every context shard and the
+// query host's cache (E4M3 context shards when k_scale is set), then the merge.
+star_status_t query_mfma(const void* q, int32_t rows, const void* k_ctx, const void* v_ctx, const float* k_scale,
+                         const float* v_scale, int64_t L, const int64_t* shard_bounds, int32_t n_shards,
+                         const void* k_tail, const void* v_tail, int64_t tail_len, int64_t tail_cap, int32_t hq,
+                         int32_t hkv, int32_t d, float scale, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, const char* who) {
+    if (L > star::attn_mfma_max_tokens(d) || tail_cap > star::attn_mfma_max_tokens(d))
+        return fail(STAR_ERR_UNSUPPORTED, "more than %lld tokens per kv head", (long long)star::attn_mfma_max_tokens(d));
+    const bool f8 = k_scale != nullptr;
+    const int eb = f8 ? 1 : 2;   // bytes per context element
+    star::PartPlan plan = {};
+    plan.n_parts = n_shards + 1;
+    for (int r = 0; r < n_shards; ++r) {
+        plan.k[r] = static_cast<const char*>(k_ctx) + shard_bounds[r] * d * eb;
+        plan.v[r] = static_cast<const char*>(v_ctx) + shard_bounds[r] * d * eb;
+        plan.head_stride[r] = L * d;
+        plan.n_kv[r] = shard_bounds[r + 1] - shard_bounds[r];
+        plan.causal[r] = -1;
+    }
+    plan.k[n_shards] = k_tail;
+    plan.v[n_shards] = v_tail;
+    plan.head_stride[n_shards] = tail_cap * d;
+    plan.n_kv[n_shards] = tail_len;
+    plan.causal[n_shards] = tail_len - rows;   // row i sees query-host tokens t <= tail_len - rows + i
+    plan.n_f8 = f8 ? n_shards : 0;
+    plan.k_scale = k_scale;
+    plan.v_scale = v_scale;
+    const int nrt = star::partial_mfma_plan(plan, rows, hq, hkv);
+    const int32_t ns = plan.split_prefix[plan.n_parts];
+    const int64_t n_max = star::partial_mfma_max_splits(rows, hq, hkv, plan.n_parts);
+    if (ns > n_max) return fail(STAR_ERR_HIP, "%s: split plan exceeds its bound", who);
+    const size_t need = partials_bytes(n_max, (int64_t)hq * rows, d);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    float *wa, *wm, *wl;
+    partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
+    hipError_t e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, d, scale, plan, nrt,
+                                             wa, wm, wl, stream);
+    if (e != hipSuccess) return hip_fail(e, who);
+    e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, o, true, lse, nullptr, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, who);
+    return ok();
+}
+
 // Chunk plan of the decode kernel and its workspace carve-up.
 struct DecodeLaunch {
     star::DecodeChunkPlan plan;
@@ -287,74 +357,54 @@ star_status_t star_phase2_query(const void* q, int32_t rows, const void* k_ctx, 
                                 int32_t d, star_dtype_t dt, float scale, void* o, float* lse, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
     try {
-        if (!q || !k_ctx || !v_ctx || !k_tail || !v_tail || !o || !shard_bounds)
-            return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
-        if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
-        if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
-        if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
-        if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
-            return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
-        for (int r = 0; r < n_shards; ++r)
-            if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
-        if (tail_len < rows || tail_len > tail_cap)
-            return fail(STAR_ERR_INVALID_ARG, "need rows <= tail_len <= tail_cap (rows %d, tail_len %lld, tail_cap %lld)",
-                        rows, (long long)tail_len, (long long)tail_cap);
-        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
-        star_status_t s = check_heads(hq, hkv, d, dt);
+        if (!k_ctx || !v_ctx) return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+        if (!aligned16(k_ctx) || !aligned16(v_ctx)) return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+        star_status_t s = check_query(q, rows, L, shard_bounds, n_shards, k_tail, v_tail, tail_len, tail_cap, hq, hkv,
+                                      d, dt, scale, o, lse);
         if (s != STAR_OK) return s;
-        if (!aligned16(q) || !aligned16(k_ctx) || !aligned16(v_ctx) || !aligned16(k_tail) || !aligned16(v_tail) ||
-            !aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-            return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
         const int64_t causal = tail_len - rows;   // row i sees query-host tokens t <= causal + i
-        hipError_t e;
-        if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
-            if (L > star::attn_mfma_max_tokens(d) || tail_cap > star::attn_mfma_max_tokens(d))
-                return fail(STAR_ERR_UNSUPPORTED, "more than %lld tokens per kv head", (long long)star::attn_mfma_max_tokens(d));
-            star::PartPlan plan = {};
-            plan.n_parts = n_shards + 1;
-            for (int r = 0; r < n_shards; ++r) {
-                plan.k[r] = static_cast<const uint16_t*>(k_ctx) + shard_bounds[r] * d;
-                plan.v[r] = static_cast<const uint16_t*>(v_ctx) + shard_bounds[r] * d;
-                plan.head_stride[r] = L * d;
-                plan.n_kv[r] = shard_bounds[r + 1] - shard_bounds[r];
-                plan.causal[r] = -1;
-            }
-            plan.k[n_shards] = static_cast<const uint16_t*>(k_tail);
-            plan.v[n_shards] = static_cast<const uint16_t*>(v_tail);
-            plan.head_stride[n_shards] = tail_cap * d;
-            plan.n_kv[n_shards] = tail_len;
-            plan.causal[n_shards] = causal;
-            const int nrt = star::partial_mfma_plan(plan, rows, hq, hkv);
-            const int32_t ns = plan.split_prefix[plan.n_parts];
-            const int64_t n_max = star::partial_mfma_max_splits(rows, hq, hkv, plan.n_parts);
-            if (ns > n_max) return fail(STAR_ERR_HIP, "star_phase2_query: split plan exceeds its bound");
-            const size_t need = partials_bytes(n_max, (int64_t)hq * rows, d);
-            if (!workspace || workspace_bytes < need || !aligned16(workspace))
-                return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
-                            workspace ? workspace_bytes : (size_t)0);
-            float *wa, *wm, *wl;
-            partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
-            e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, d, scale, plan, nrt,
-                                          wa, wm, wl, stream);
-            if (e != hipSuccess) return hip_fail(e, "star_phase2_query launch");
-            e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, o, true, lse, nullptr, nullptr, stream);
-            if (e != hipSuccess) return hip_fail(e, "star_phase2_query merge launch");
-        } else {
-            star::RowAttnArgs a = {};
-            a.q = q; a.q_rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
-            a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 1;
-            a.n_seg = 2;
-            a.seg[0].k = k_ctx; a.seg[0].v = v_ctx; a.seg[0].head_stride = L * d;
-            a.seg[0].n = L; a.seg[0].causal_lim = -1;
-            a.seg[1].k = k_tail; a.seg[1].v = v_tail; a.seg[1].head_stride = tail_cap * d;
-            a.seg[1].n = tail_len; a.seg[1].causal_lim = causal;
-            a.o = o; a.lse = lse;
-            e = star::launch_row_attn(a, rows, stream);
-            if (e != hipSuccess) return hip_fail(e, "star_phase2_query launch");
-        }
+        if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv))
+            return query_mfma(q, rows, k_ctx, v_ctx, nullptr, nullptr, L, shard_bounds, n_shards, k_tail, v_tail,
+                              tail_len, tail_cap, hq, hkv, d, scale, o, lse, workspace, workspace_bytes, stream,
+                              "star_phase2_query");
+        star::RowAttnArgs a = {};
+        a.q = q; a.q_rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
+        a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 1;
+        a.n_seg = 2;
+        a.seg[0].k = k_ctx; a.seg[0].v = v_ctx; a.seg[0].head_stride = L * d;
+        a.seg[0].n = L; a.seg[0].causal_lim = -1;
+        a.seg[1].k = k_tail; a.seg[1].v = v_tail; a.seg[1].head_stride = tail_cap * d;
+        a.seg[1].n = tail_len; a.seg[1].causal_lim = causal;
+        a.o = o; a.lse = lse;
+        const hipError_t e = star::launch_row_attn(a, rows, stream);
+        if (e != hipSuccess) return hip_fail(e, "star_phase2_query launch");
         return ok();
     } catch (...) {
         return fail(STAR_ERR_HIP, "star_phase2_query: internal error");
+    }
+}
+
+star_status_t star_phase2_query_kv8(const void* q, int32_t rows, const void* k_ctx8, const void* v_ctx8,
+                                    const float* k_scale, const float* v_scale, int64_t L,
+                                    const int64_t* shard_bounds, int32_t n_shards, const void* k_tail,
+                                    const void* v_tail, int64_t tail_len, int64_t tail_cap, int32_t hq, int32_t hkv,
+                                    int32_t d, star_dtype_t dt, float scale, void* o, float* lse, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    try {
+        if (!k_ctx8 || !v_ctx8 || !k_scale || !v_scale) return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+        if (!aligned16(k_ctx8) || !aligned16(v_ctx8) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+            (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+            return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned (scales 4-byte)");
+        star_status_t s = check_query(q, rows, L, shard_bounds, n_shards, k_tail, v_tail, tail_len, tail_cap, hq, hkv,
+                                      d, dt, scale, o, lse);
+        if (s != STAR_OK) return s;
+        if (dt != STAR_BF16 || !star::attn_mfma_supported(d, hq, hkv))
+            return fail(STAR_ERR_UNSUPPORTED, "E4M3 context query needs bf16, d = 64 or 128 and hq/hkv dividing 256");
+        return query_mfma(q, rows, k_ctx8, v_ctx8, k_scale, v_scale, L, shard_bounds, n_shards, k_tail, v_tail,
+                          tail_len, tail_cap, hq, hkv, d, scale, o, lse, workspace, workspace_bytes, stream,
+                          "star_phase2_query_kv8");
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_phase2_query_kv8: internal error");
     }
 }
 

@@ -233,9 +233,9 @@ star_status_t star_decode_step(const void *q_new, const void *k_new, const void 
  * 3 mantissa bits, largest finite 448, S.1111.111 = NaN) with one fp32 scale
  * per kv head for K and one for V; the cached value is scale * decode(code).
  * The query host's cache stays in the compute dtype.  A typical order: Phase
- * 1, then the query phase on the bf16 cache, then star_kv_fp8_scales and
- * star_kv_quantize_fp8 on each context tensor, then star_decode_step_kv8 per
- * generated token.
+ * 1, then star_kv_fp8_scales and star_kv_quantize_fp8 on each context tensor,
+ * then the query phase (star_phase2_query, or star_phase2_query_kv8 on the
+ * codes) and star_decode_step_kv8 per generated token.
  *
  * star_kv_fp8_scales: scale[g] = max |x[g]| / 448 in fp32 (1 for a head that
  * is all zeros), so each head's largest element maps to +-448.
@@ -258,6 +258,31 @@ star_status_t star_kv_fp8_scales(const void *x, int64_t tokens, int32_t hkv, int
 star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32_t hkv, int32_t d,
                                    star_dtype_t dt, const float *scale, void *out,
                                    hipStream_t stream);
+
+/*
+ * Phase 2 query encoding over an E4M3 context cache.
+ * [SUM] 3.4 Phase 2 Steps 1-5 over the dequantised context (see above).
+ *
+ * Arguments and behaviour as star_phase2_query, except:
+ *   k_ctx8, v_ctx8 [hkv, L, d] uint8 E4M3 codes (16-byte aligned) replace
+ *   k_ctx / v_ctx; k_scale, v_scale [hkv] fp32 (device, 4-byte aligned) are
+ *   their scales.  dt must be STAR_BF16 (q, the query-host cache and o), d 64
+ *   or 128 and hq/hkv a divisor of 256; other shapes return
+ *   STAR_ERR_UNSUPPORTED.  The workspace is
+ *   star_phase2_query_workspace_bytes(...) bytes, with the same rules.  Two
+ *   kernel launches as star_phase2_query's bf16 path; the context tiles are
+ *   widened exactly to bf16 on their way into LDS.
+ */
+star_status_t star_phase2_query_kv8(const void *q, int32_t rows,
+                                    const void *k_ctx8, const void *v_ctx8,
+                                    const float *k_scale, const float *v_scale, int64_t L,
+                                    const int64_t *shard_bounds, int32_t n_shards,
+                                    const void *k_tail, const void *v_tail,
+                                    int64_t tail_len, int64_t tail_cap,
+                                    int32_t hq, int32_t hkv, int32_t d,
+                                    star_dtype_t dt, float scale,
+                                    void *o, float *lse,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Phase 2, one generated token over an E4M3 context cache.

@@ -18,8 +18,9 @@ given there, so the following reading is taken:
 * dequantisation: value = scale * decode(code), exact in float64;
 * default scale of a kv head: its largest |x| divided by 448 in fp32 (1 when
   the head is all zeros), so the largest element maps to +-448;
-* a decode step over a quantised context is the plain Phase-2 decode step
-  (section 3.4, Phase 2 Steps 3-5 and 7) over the dequantised values.
+* the query phase and a decode step over a quantised context are the plain
+  Phase-2 query phase (section 3.4, Phase 2 Steps 1-5) and decode step (Steps
+  3-5 and 7) over the dequantised values.
 
 The E4M3 format itself is the OCP 8-bit floating point specification's: one
 sign bit, four exponent bits with bias 7, three mantissa bits; exponent field 0
@@ -95,14 +96,20 @@ def kv_dequantize(codes, scale) -> np.ndarray:
     return s * e4m3_decode(c)
 
 
+def _dequantized_cache(k8, v8, k_scale, v_scale):
+    """The context cache's values: K with the K scales, V with the V scales (float64)."""
+    kd = np.ascontiguousarray(kv_dequantize(k8, k_scale))
+    vd = np.ascontiguousarray(kv_dequantize(v8, v_scale))
+    return kd, vd
+
+
 def phase2_decode_kv8(q_t, k8, v8, k_scale, v_scale, shard_bounds, k_tail, v_tail, tail_len,
                       scale=None, threads=None):
     """One generated token over an E4M3 context cache: q_t [Hq, d] attends to every context
     shard of the dequantised k8/v8 [Hkv, L, d] and to the query host's cache
     k_tail/v_tail [Hkv, >=tail_len, d] (compute dtype), which already holds the new
     token's own k/v at index tail_len - 1.  Returns (O [Hq, d], LSE [Hq]) in float64."""
-    kd = np.ascontiguousarray(kv_dequantize(k8, k_scale))
-    vd = np.ascontiguousarray(kv_dequantize(v8, v_scale))
+    kd, vd = _dequantized_cache(k8, v8, k_scale, v_scale)
     q3 = np.ascontiguousarray(widen(q_t)[:, None, :])
     kt = np.ascontiguousarray(widen(k_tail))
     vt = np.ascontiguousarray(widen(v_tail))
@@ -113,3 +120,24 @@ def phase2_decode_kv8(q_t, k8, v8, k_scale, v_scale, shard_bounds, k_tail, v_tai
     o, lse = merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]),
                    np.stack([p[2] for p in parts]))
     return o[:, 0, :], lse[:, 0]
+
+
+def phase2_query_kv8(q_qry, k8, v8, k_scale, v_scale, shard_bounds, k_tail, v_tail, tail_len,
+                     scale=None, threads=None):
+    """Query encoding over an E4M3 context cache: the rows of q_qry [Hq, rows, d] are the last
+    rows of the query host's cache k_tail/v_tail [Hkv, >=tail_len, d] (compute dtype), so
+    row i sees cache positions [0, tail_len - rows + i] causally, and every token of every
+    context shard of the dequantised k8/v8 [Hkv, L, d].  One partial per context shard plus
+    the query host's own partial, merged.  Returns (O [Hq, rows, d], LSE [Hq, rows])."""
+    kd, vd = _dequantized_cache(k8, v8, k_scale, v_scale)
+    q3 = np.ascontiguousarray(widen(q_qry))
+    kt = np.ascontiguousarray(widen(k_tail))
+    vt = np.ascontiguousarray(widen(v_tail))
+    rows = q3.shape[1]
+    assert _as_input(kd)[1] == _as_input(q3)[1] == _as_input(kt)[1]
+    assert rows <= int(tail_len) <= kt.shape[1]
+    parts = [partial(q3, kd, vd, int(lo), int(hi), -1, scale, threads)
+             for lo, hi in zip(shard_bounds[:-1], shard_bounds[1:])]
+    parts.append(partial(q3, kt, vt, 0, int(tail_len), int(tail_len) - rows, scale, threads))
+    return merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]),
+                 np.stack([p[2] for p in parts]))

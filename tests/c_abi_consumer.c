@@ -48,6 +48,10 @@ int main(void) {
     expect(star_decode_step_kv8(fake, fake, fake, fake, fake, fake, fake, 100, bounds, 2, fake, fake, 0, 8, 4, 2, 96,
                                 STAR_BF16, 0.1f, fake, NULL, fake, (size_t)1 << 30, 0) == STAR_ERR_UNSUPPORTED,
            "E4M3 decode rejects head dim 96");
+    expect(star_phase2_query_kv8(fake, 8, fake, fake, (const float *)fake, (const float *)fake, 100, bounds, 2, fake,
+                                 fake, 8, 8, 4, 2, 128, STAR_F32, 0.1f, fake, NULL, fake, (size_t)1 << 30, 0) ==
+               STAR_ERR_UNSUPPORTED,
+           "E4M3 query rejects fp32");
     expect(star_kv_fp8_scales(fake, 100, 8, 100, STAR_BF16, (float *)fake, 0) == STAR_ERR_UNSUPPORTED,
            "E4M3 scales reject d % 8 != 0");
     expect(star_softmax_merge((const float *)fake, (const float *)fake, (const float *)fake, 0, 4, 1, 128, fake,

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -124,6 +124,25 @@ def test_decode_kv8_validation(lib):
     assert d(*args(dim=96)) == 2                           # head dim 96
     assert d(*args(hq=6, hkv=2)) == 2                      # G = 3
     assert d(*args(ws=16)) == 4                            # workspace too small
+
+
+def test_query_kv8_validation(lib):
+    q = lib.star_phase2_query_kv8
+    B = ctypes.c_int64 * 3
+    good = B(0, 50, 100)
+
+    def args(bounds=good, ks=FAKE, k8=FAKE, hq=4, hkv=2, dim=128, dt=1, rows=8, tl=8, tc=8, ws=1 << 30):
+        return (FAKE, rows, k8, FAKE, ks, FAKE, 100, bounds, 2, FAKE, FAKE, tl, tc, hq, hkv, dim, dt, 0.1,
+                FAKE, NULL, FAKE, ws, NULL)
+    assert q(*args(ks=NULL)) == 1                          # null scale
+    assert q(*args(k8=NULL)) == 1                          # null codes
+    assert q(*args(k8=ctypes.c_void_p(0x100008))) == 1     # misaligned codes
+    assert q(*args(bounds=B(0, 60, 50))) == 1              # not monotone
+    assert q(*args(tl=7)) == 1                             # fewer cached tokens than rows
+    assert q(*args(dt=0)) == 2                             # fp32: no E4M3 path
+    assert q(*args(dim=96)) == 2                           # head dim 96
+    assert q(*args(hq=6, hkv=2)) == 2                      # G = 3
+    assert q(*args(ws=16)) == 4                            # workspace too small
 
 
 def test_query_validation(lib):

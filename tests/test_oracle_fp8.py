@@ -152,3 +152,56 @@ def test_kv8_decode_against_dense_softmax(scale):
         w = np.exp(x - x.max())
         np.testing.assert_allclose(o8[h], w @ vals / w.sum(), rtol=0, atol=1e-12)
         np.testing.assert_allclose(l8[h], x.max() + np.log(w.sum()), rtol=1e-13)
+
+
+def test_kv8_query_equals_plain_oracle_on_fp32_exact_values():
+    """Power-of-two scales (different per head and between K and V) make the dequantised
+    context fp32-exact: the E4M3 query phase must equal the plain oracle's query phase on
+    those values, and swapping the heads' V scales must change it."""
+    rng = np.random.default_rng(19)
+    hq, hkv, L, d, lq = 8, 2, 260, 32, 7
+    k8 = rng.integers(0, 256, (hkv, L, d)).astype(np.uint8)
+    v8 = rng.integers(0, 256, (hkv, L, d)).astype(np.uint8)
+    for c in (k8, v8):
+        c[(c & 0x7F) == 0x7F] ^= 1
+    ks = np.float32([2.0 ** -5, 2.0 ** -3])
+    vs = np.float32([2.0 ** 2, 2.0 ** -1])
+    q = rng.standard_normal((hq, lq, d)).astype(np.float32)
+    kt = rng.standard_normal((hkv, lq, d)).astype(np.float32)
+    vt = rng.standard_normal((hkv, lq, d)).astype(np.float32)
+    bounds = [0, 90, 90, 260]
+    o8, l8 = f8.phase2_query_kv8(q, k8, v8, ks, vs, bounds, kt, vt, lq)
+    kd = f8.kv_dequantize(k8, ks).astype(np.float32)
+    vd = f8.kv_dequantize(v8, vs).astype(np.float32)
+    o, l = oracle.phase2_query(q, kd, vd, bounds, kt, vt)
+    np.testing.assert_allclose(o8, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l8, l, rtol=1e-14, atol=0)
+    o_sw, _ = f8.phase2_query_kv8(q, k8, v8, ks, vs[::-1].copy(), bounds, kt, vt, lq)
+    assert np.abs(o_sw - o).max() > 1e-3
+
+
+def test_kv8_query_rows_after_cached_tokens_against_dense_softmax():
+    """Brute force: query rows that are the last 3 of 8 cached tokens see the whole
+    dequantised context and the cache causally (row i up to position 5 + i), one dense
+    softmax per row."""
+    rng = np.random.default_rng(23)
+    hq, hkv, L, d, rows, tail_len, cap = 6, 3, 30, 16, 3, 8, 11
+    k8 = rng.integers(0, 0x7E, (hkv, L, d)).astype(np.uint8) | (rng.integers(0, 2, (hkv, L, d)) << 7).astype(np.uint8)
+    v8 = rng.integers(0, 0x7E, (hkv, L, d)).astype(np.uint8) | (rng.integers(0, 2, (hkv, L, d)) << 7).astype(np.uint8)
+    ks, vs = np.float32([0.01, 0.02, 0.004]), np.float32([0.03, 0.005, 0.1])
+    q = rng.standard_normal((hq, rows, d)).astype(np.float32)
+    kt = rng.standard_normal((hkv, cap, d)).astype(np.float32)
+    vt = rng.standard_normal((hkv, cap, d)).astype(np.float32)
+    o8, l8 = f8.phase2_query_kv8(q, k8, v8, ks, vs, [0, 11, 30], kt, vt, tail_len)
+    sc = 1 / np.sqrt(d)
+    G = hq // hkv
+    for h in range(hq):
+        g = h // G
+        for i in range(rows):
+            vis = tail_len - rows + i + 1
+            keys = np.concatenate([float(ks[g]) * f8.e4m3_decode(k8[g]), kt[g, :vis].astype(np.float64)])
+            vals = np.concatenate([float(vs[g]) * f8.e4m3_decode(v8[g]), vt[g, :vis].astype(np.float64)])
+            x = sc * keys @ q[h, i].astype(np.float64)
+            w = np.exp(x - x.max())
+            np.testing.assert_allclose(o8[h, i], w @ vals / w.sum(), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(l8[h, i], x.max() + np.log(w.sum()), rtol=1e-13)

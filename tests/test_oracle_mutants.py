@@ -90,6 +90,10 @@ FP8_MUTANTS = {
     "sign_dropped": ("code = np.where(np.isnan(x), 0x7F, pick) | sign", "code = np.where(np.isnan(x), 0x7F, pick)"),
     "v_takes_k_scale": ("vd = np.ascontiguousarray(kv_dequantize(v8, v_scale))",
                         "vd = np.ascontiguousarray(kv_dequantize(v8, k_scale))"),
+    "query_tail_not_causal": ("parts.append(partial(q3, kt, vt, 0, int(tail_len), int(tail_len) - rows, scale, threads))",
+                              "parts.append(partial(q3, kt, vt, 0, int(tail_len), -1, scale, threads))"),
+    "query_tail_offset_off_by_one": ("int(tail_len) - rows, scale, threads))",
+                                     "int(tail_len) - rows - 1, scale, threads))"),
     "quantize_multiplies": ("qv = (v / s).astype(np.float32)", "qv = (v * s).astype(np.float32)"),
     "absmax_over_256": ("s = (amax.astype(np.float32) / np.float32(E4M3_MAX))",
                         "s = (amax.astype(np.float32) / np.float32(256.0))"),
@@ -103,7 +107,9 @@ def _fp8_pin_calls():
                 p8.test_encode_round_trips_every_finite_code, p8.test_rounding_error_within_half_a_step,
                 p8.test_absmax_scales_map_each_heads_largest_element_to_448,
                 p8.test_kv8_decode_equals_plain_oracle_on_fp32_exact_values,
-                lambda: p8.test_kv8_decode_against_dense_softmax(None)]
+                lambda: p8.test_kv8_decode_against_dense_softmax(None),
+                p8.test_kv8_query_equals_plain_oracle_on_fp32_exact_values,
+                p8.test_kv8_query_rows_after_cached_tokens_against_dense_softmax]
 
 
 def test_fp8_pins_pass_on_the_real_module():

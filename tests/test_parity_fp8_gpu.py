@@ -1,6 +1,6 @@
 """GPU parity of the E4M3 context cache: scales and codes bit-exact against the oracle, and
-the decode step over an E4M3 context (codes and scales made by the oracle) against the
-oracle's decode over the dequantised values."""
+the query phase and the decode step over an E4M3 context (codes and scales made by the
+oracle) against the oracle's over the dequantised values."""
 import numpy as np
 import pytest
 import torch
@@ -136,6 +136,56 @@ def test_decode_kv8_equals_bf16_decode_on_representable_values():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("hq,hkv,L,bounds,rows,tail_len,tail_cap,d", [
+    (8, 2, 3000, [0, 800, 1600, 3000], 40, 40, 48, 128),             # G = 4, ragged shards
+    (16, 1, 2333, [0, 700, 700, 2333], 9, 30, 33, 64),               # d = 64, G = 16, an empty shard
+    (4, 4, 777, [0, 777], 1, 1, 1, 128),                              # G = 1, one row, one cached token
+    (16, 2, 1500, [0, 512, 1024, 1500], 20, 20, 24, 128),             # G = 8
+    (8, 1, 6000, [0, 1500, 3000, 4500, 6000], 300, 300, 310, 128),    # several row tiles and key splits
+    (4, 2, 100, [0, 37, 100], 70, 70, 70, 64),                        # context shorter than two tiles
+])
+def test_query_kv8(hq, hkv, L, bounds, rows, tail_len, tail_cap, d):
+    """The query phase over an E4M3 context cache (oracle-made codes and scales) against the
+    oracle's query phase over the dequantised context; the query host's cache is bf16."""
+    flush_print("query kv8", hq, hkv, L, bounds, rows, tail_len, d)
+    cfg = _cfg(hq, hkv, L, L, d=d, lq=tail_len, T=1, S=len(bounds) - 1, seed=89)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    k8, v8, ks, vs, (hk8, hv8, hks, hvs) = _oracle_cache(k, v)
+    qr = p2["q_qry"][:, tail_len - rows:].contiguous()
+    k_tail = torch.zeros((hkv, tail_cap, d), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :tail_len] = p2["k_qry"]
+    v_tail[:, :tail_len] = p2["v_qry"]
+    o, lse = sa.star_phase2_query_kv8(qr, k8, v8, ks, vs, bounds, k_tail, v_tail, tail_len)
+    torch.cuda.synchronize()
+    ro, rl = of8.phase2_query_kv8(qr.cpu(), hk8, hv8, hks, hvs, bounds, k_tail.cpu(), v_tail.cpu(), tail_len)
+    assert_out(o, ro, "kv8 query O")
+    assert_lse(lse, rl, "kv8 query LSE")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_query_kv8_equals_bf16_query_on_representable_values(d):
+    """With unit scales and a context whose bf16 values are E4M3 values, the E4M3 query phase
+    and the bf16 query phase compute the same numbers: bit-identical outputs."""
+    cfg = _cfg(8, 2, 2000, 2000, d=d, lq=24, T=1, S=2, seed=97)
+    _, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    one = np.float32([1.0, 1.0])
+    hk8 = of8.kv_quantize(k.cpu(), one)
+    hv8 = of8.kv_quantize(v.cpu(), one)
+    kr = torch.from_numpy(of8.e4m3_decode(hk8).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    vr = torch.from_numpy(of8.e4m3_decode(hv8).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    ones = torch.ones(2, dtype=torch.float32, device=DEV)
+    bounds = [0, 900, 2000]
+    k_tail, v_tail = p2["k_qry"].contiguous(), p2["v_qry"].contiguous()
+    o8, l8 = sa.star_phase2_query_kv8(p2["q_qry"], torch.from_numpy(hk8).to(DEV), torch.from_numpy(hv8).to(DEV),
+                                      ones, ones, bounds, k_tail, v_tail, 24)
+    ob, lb = sa.star_phase2_query(p2["q_qry"], kr, vr, bounds, k_tail, v_tail, 24)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, ob) and torch.equal(l8, lb)
+
+
 def test_quantize_and_kv8_decode_replayed_from_a_hip_graph():
     """The scales, the quantisation of K and V and T E4M3 decode steps, captured in one HIP
     graph (the library allocates nothing and records no memsets), replay bit-identically to
@@ -219,6 +269,17 @@ def test_decode_kv8_full(name):
     v_tail = torch.zeros_like(k_tail)
     k_tail[:, :cfg.lq] = x["k_qry"]
     v_tail[:, :cfg.lq] = x["v_qry"]
+    # the query phase over the E4M3 cache, checked on its first and last 16 rows: the first
+    # rows see a cache of 16 tokens, the last ones the whole query
+    oq, lq_lse = sa.star_phase2_query_kv8(x["q_qry"], k8, v8, ks, vs, bounds, k_tail, v_tail, cfg.lq)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lq_lse).all())
+    kt, vt = k_tail.cpu(), v_tail.cpu()
+    for lo, tl in ((0, 16), (cfg.lq - 16, cfg.lq)):
+        ro, rl = of8.phase2_query_kv8(x["q_qry"][:, lo:lo + 16].cpu(), hk8, hv8, hks, hvs, bounds, kt, vt, tl)
+        assert_out(oq[:, lo:lo + 16], ro, "%s kv8 query rows %d.. O" % (name, lo))
+        assert_lse(lq_lse[:, lo:lo + 16], rl, "%s kv8 query rows %d.. LSE" % (name, lo))
+    flush_print("  kv8 query ok")
     T = cfg.decode_steps
     ws = sa.decode_workspace(cfg.L, cfg.tail_cap, cfg.shards, cfg.hq, cfg.hkv, cfg.d, DEV)
     od = torch.empty((T, cfg.hq, cfg.d), dtype=torch.bfloat16, device=DEV)
