@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 METRIC = "Phase-1 context tokens/s + MFMA %peak; Phase-2 decode KV GB/s (%HBM), 1 GPU"
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
-PHASE1_KERNEL = "attn_mfma_kernel<0, 128>"
+PHASE1_KERNEL = "attn_mfma_kernel<0, 128, false>"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "phase1_8b_32k_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_phase1_amd", "csrc", f)
                   for f in ("prefill.hip", "common.h", "internal.h")]

@@ -76,6 +76,25 @@ DECODE = _decode_cases(12)
 QUERY = _query_cases(8)
 
 
+def _query_kv8_cases(n):
+    """E4M3 context query cases from a generator of their own (the lists above stay as drawn)."""
+    rng = random.Random(20241204)
+    out = []
+    for _ in range(n):
+        hkv = rng.choice([1, 2, 4])
+        G = rng.choice([1, 2, 4, 8, 16])
+        d = rng.choice([64, 128])
+        L = rng.randint(1, 4000)
+        S = rng.randint(1, 5)
+        tail_len = rng.randint(1, 300)
+        rows = rng.randint(1, tail_len)
+        out.append((hkv * G, hkv, L, _bounds(rng, L, S), rows, tail_len, d))
+    return out
+
+
+QUERY8 = _query_kv8_cases(8)
+
+
 def _cfg(hq, hkv, L, d, lq=4, T=1, seed=1):
     return StarConfig("sweep", hq=hq, hkv=hkv, d=d, L=L, block=L, anchor=L, lq=max(lq, 1), decode_steps=T,
                       shards=1, dtype="bf16", needle=False, seed=seed)
@@ -115,6 +134,29 @@ def test_sweep_query(i):
     parts.append(oracle.partial(qc, kt.cpu(), vt.cpu(), 0, tail_len, tail_len - rows))
     ro, rl = oracle.merge(np.stack([x[0] for x in parts]), np.stack([x[1] for x in parts]),
                           np.stack([x[2] for x in parts]))
+    assert_out(o, ro, "O %s" % (case,))
+    assert_lse(lse, rl, "LSE %s" % (case,))
+
+
+@pytest.mark.parametrize("i", range(len(QUERY8)), ids=[str(c) for c in QUERY8])
+def test_sweep_query_kv8(i):
+    case = QUERY8[i]
+    hq, hkv, L, bounds, rows, tail_len, d = case
+    flush_print("sweep query kv8", case)
+    cfg = _cfg(hq, hkv, L, d, lq=tail_len, seed=600 + i)
+    _, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    qr = p2["q_qry"][:, tail_len - rows:].contiguous()
+    kt = torch.zeros((hkv, tail_len + 3, d), dtype=torch.bfloat16, device=DEV)
+    vt = torch.zeros_like(kt)
+    kt[:, :tail_len] = p2["k_qry"]
+    vt[:, :tail_len] = p2["v_qry"]
+    ks, vs = of8.kv_absmax_scales(k.cpu()), of8.kv_absmax_scales(v.cpu())
+    hk8, hv8 = of8.kv_quantize(k.cpu(), ks), of8.kv_quantize(v.cpu(), vs)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    o, lse = sa.star_phase2_query_kv8(qr, to(hk8), to(hv8), to(ks), to(vs), bounds, kt, vt, tail_len)
+    torch.cuda.synchronize()
+    ro, rl = of8.phase2_query_kv8(qr.cpu(), hk8, hv8, ks, vs, bounds, kt.cpu(), vt.cpu(), tail_len)
     assert_out(o, ro, "O %s" % (case,))
     assert_lse(lse, rl, "LSE %s" % (case,))
 
