@@ -355,8 +355,20 @@ def cpu_baseline(cfg, q, k, v, seconds):
         done += batch
         batch = min(batch * 2, 1024)
     return {"value": done / elapsed, "unit": "context tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d seeded-random Phase-1 context rows x all %d q heads of %s, fp64 C oracle, %.1f s"
-                      % (done, cfg.hq, cfg.name, elapsed)}
+            "sample": "%d seeded-random Phase-1 context rows x all %d q heads of %s, fp64 C oracle, %.1f s on %s"
+                      % (done, cfg.hq, cfg.name, elapsed, cpu_model())}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 if __name__ == "__main__":

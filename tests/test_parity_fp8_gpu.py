@@ -187,9 +187,9 @@ def test_query_kv8_equals_bf16_query_on_representable_values(d):
 
 
 def test_quantize_and_kv8_decode_replayed_from_a_hip_graph():
-    """The scales, the quantisation of K and V and T E4M3 decode steps, captured in one HIP
-    graph (the library allocates nothing and records no memsets), replay bit-identically to
-    the eager calls, with eager work between the replays."""
+    """The scales, the quantisation of K and V, the query phase and T decode steps over the
+    E4M3 cache, captured in one HIP graph (the library allocates nothing and records no
+    memsets), replay bit-identically to the eager calls, with eager work between the replays."""
     cfg = _cfg(8, 2, 3000, 3000, lq=16, T=3, S=3, seed=89)
     q, k, v = sin.phase1_inputs(cfg, DEV)
     p2 = sin.phase2_inputs(cfg, DEV)
@@ -206,6 +206,10 @@ def test_quantize_and_kv8_decode_replayed_from_a_hip_graph():
                     k8=torch.empty(k.shape, dtype=torch.uint8, device=DEV),
                     v8=torch.empty(v.shape, dtype=torch.uint8, device=DEV), kt=kt, vt=vt,
                     ws=sa.decode_workspace(cfg.L, cap, 3, cfg.hq, cfg.hkv, d, DEV),
+                    wq=torch.empty(max(16, sa.star_phase2_query_workspace_bytes(lq, 3, cfg.hq, cfg.hkv, d)),
+                                   dtype=torch.uint8, device=DEV),
+                    oq=torch.empty((cfg.hq, lq, d), dtype=torch.bfloat16, device=DEV),
+                    lq=torch.empty((cfg.hq, lq), dtype=torch.float32, device=DEV),
                     o=[torch.empty((cfg.hq, d), dtype=torch.bfloat16, device=DEV) for _ in range(T)],
                     l=[torch.empty((cfg.hq,), dtype=torch.float32, device=DEV) for _ in range(T)])
 
@@ -214,6 +218,8 @@ def test_quantize_and_kv8_decode_replayed_from_a_hip_graph():
         sa.star_kv_quantize_fp8(k, b["ks"], b["k8"])
         sa.star_kv_fp8_scales(v, b["vs"])
         sa.star_kv_quantize_fp8(v, b["vs"], b["v8"])
+        sa.star_phase2_query_kv8(p2["q_qry"], b["k8"], b["v8"], b["ks"], b["vs"], bounds, b["kt"], b["vt"], lq,
+                                 o=b["oq"], lse=b["lq"], workspace=b["wq"])
         for t in range(T):
             sa.star_decode_step_kv8(p2["q_dec"][t], p2["k_dec"][t], p2["v_dec"][t], b["k8"], b["v8"], b["ks"], b["vs"],
                                     bounds, b["kt"], b["vt"], lq + t, o=b["o"][t], lse=b["l"][t], workspace=b["ws"])
@@ -228,14 +234,14 @@ def test_quantize_and_kv8_decode_replayed_from_a_hip_graph():
     for rep in range(3):
         graph.replay()
         torch.cuda.synchronize()
-        for name in ("ks", "vs", "k8", "v8", "kt", "vt"):
+        for name in ("ks", "vs", "k8", "v8", "kt", "vt", "oq", "lq"):
             assert torch.equal(g[name], eager[name]), "replay %d: %s differs" % (rep, name)
         for t in range(T):
             assert torch.equal(g["o"][t], eager["o"][t]), "replay %d step %d: O differs" % (rep, t)
             assert torch.equal(g["l"][t], eager["l"][t]), "replay %d step %d: LSE differs" % (rep, t)
         # unrelated eager work between replays, and outputs cleared
         sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor)
-        for name in ("ks", "vs", "k8", "v8"):
+        for name in ("ks", "vs", "k8", "v8", "oq", "lq"):
             g[name].zero_()
         for t in range(T):
             g["o"][t].zero_()
