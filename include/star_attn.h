@@ -94,7 +94,10 @@ const char *star_version(void);
  *   o    [hq, L, d]    output (dt, round-to-nearest-even)
  *   lse  [hq, L]       fp32 log-sum-exp of each row's scores, or NULL
  *   L >= 1, block >= 1, 0 <= anchor <= block.
- * One kernel launch.
+ * One kernel launch: bf16 with d = 64 or 128 and hq/hkv a divisor of 256 run
+ * the MFMA kernel, which addresses a kv head with 32-bit offsets and so takes
+ * at most 2^31 / d tokens (more returns STAR_ERR_UNSUPPORTED); fp32 and other
+ * head dims (d % 4 == 0, d <= 256) run the vector kernel.
  */
 star_status_t star_phase1_encode(const void *q, const void *k, const void *v,
                                  void *o, float *lse,
@@ -118,7 +121,9 @@ star_status_t star_phase1_encode(const void *q, const void *k, const void *v,
  *   a_out [hq, rows, d], m_out [hq, rows], l_out [hq, rows]: fp32 (A, m, l).
  *   workspace: star_phase2_workspace_bytes(rows, n_kv, hq, hkv, d) bytes
  *         (may be 0, then workspace may be NULL).
- * One or two kernel launches (a key-split pass and its merge).
+ * One or two kernel launches (a key-split pass and its merge).  Shapes and the
+ * 2^31 / d token limit of the MFMA kernel as for star_phase1_encode (n_kv
+ * counts the tokens).
  */
 size_t star_phase2_workspace_bytes(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv, int32_t d);
 

@@ -54,6 +54,8 @@ NULL = ctypes.c_void_p(0)
     ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 7, 0.1), 1),          # bad dtype
     ((ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 1, 0.1), 1),  # misaligned
     ((FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 1, float("inf")), 1),  # bad scale
+    ((FAKE, FAKE, FAKE, FAKE, NULL, (1 << 24) + 1, 32, 32, 4, 2, 128, 1, 0.1), 2),  # > 2^31/d tokens (MFMA)
+    ((FAKE, FAKE, FAKE, FAKE, NULL, (1 << 25) + 1, 32, 32, 4, 2, 64, 1, 0.1), 2),   # > 2^31/d tokens, d = 64
 ])
 def test_phase1_validation(lib, args, expect):
     st = lib.star_phase1_encode(*args, NULL)
@@ -72,6 +74,9 @@ def test_partial_and_merge_validation(lib):
     assert need > 0
     assert p(FAKE, 128, FAKE, FAKE, big * 128, big, -1, 32, 8, 128, 1, 0.1, FAKE, FAKE, FAKE,
              FAKE, need - 1, NULL) == 4
+    over = (1 << 24) + 1   # one token past the MFMA kernel's 32-bit offsets at d = 128
+    assert p(FAKE, 4, FAKE, FAKE, over * 128, over, -1, 4, 2, 128, 1, 0.1, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+             NULL) == 2
     m = lib.star_softmax_merge
     assert m(FAKE, FAKE, FAKE, 0, 4, 1, 128, FAKE, 1, NULL, NULL) == 1
     assert m(FAKE, FAKE, FAKE, 2, 4, 1, 6, FAKE, 1, NULL, NULL) == 2
@@ -157,6 +162,7 @@ def test_query_validation(lib):
     assert q(*args(8, good, 2, 7, 8, 1 << 30)) == 1                  # fewer cached tokens than rows
     assert q(*args(8, good, 2, 9, 8, 1 << 30)) == 1                  # tail_len > tail_cap
     assert q(*args(8, good, 65, 8, 8, 1 << 30)) == 1                 # too many shards
+    assert q(*args(8, good, 2, 8, (1 << 24) + 1, 1 << 30)) == 2      # cache past the 32-bit offsets
     assert q(*args(8, good, 2, 8, 8, 16)) == 4                       # workspace too small
     a = list(args(8, good, 2, 8, 8, 1 << 30))
     a[0] = NULL
