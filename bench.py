@@ -41,11 +41,20 @@ KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_phase1_amd", "csrc", f)
                   for f in ("prefill.hip", "common.h", "internal.h")]
 
 
+def code_text(text: str) -> str:
+    """C++ source with comments removed and white space collapsed: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """sha256 prefix of the Phase-1 kernel's sources without comments, so that the committed
+    counter profile stays valid across comment edits and no longer after a code change."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

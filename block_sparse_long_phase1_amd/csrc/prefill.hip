@@ -24,12 +24,15 @@
 //
 // Tiles of 64 keys go through a ring of four LDS stages, copied there by direct
 // global-to-LDS loads, which take no registers and no LDS store instructions;
-// the copy of tile j+3 is in flight while tile j is multiplied.  Each tile runs
-// as two 32-key halves so that one half's exponentials issue between the other
-// half's MFMAs.  Softmax runs in the exp2 domain with a lazily updated
-// reference max: the accumulators are only rescaled when a row's max grows by
-// more than 2^8, which keeps every probability below 256 and is exact after
-// the final normalisation.
+// the copy of tile j+3 is in flight while tile j is multiplied.  (Partitions of
+// E4M3 codes instead load the codes into registers three tiles ahead and write
+// them, widened to bf16, into the same stage layout.)  Each tile runs as two
+// 32-key halves so that one half's exponentials issue between the other half's
+// MFMAs.  Softmax runs in the exp2 domain with a lazily updated reference max:
+// Phase-2 partials rescale the accumulators only when a row's max grows by more
+// than 2^8; Phase 1 keeps a half-tile when each row's probability sum over it is
+// at most 2^20 and otherwise redoes it against a moved reference.  Either way
+// the result is exact after the final normalisation.
 #include "common.h"
 #include "internal.h"
 
