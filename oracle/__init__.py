@@ -68,7 +68,8 @@ def _load():
 
 
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 64))
+    """Host threads for the oracle: the cores present, at most 16 (one GPU's share of a host)."""
+    return max(1, min(os.cpu_count() or 1, 16))
 
 
 def _as_input(x):

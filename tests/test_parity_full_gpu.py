@@ -13,7 +13,7 @@ import torch
 import block_sparse_long_phase1_amd as sa
 import oracle
 from block_sparse_long_phase1_amd import inputs as sin
-from block_sparse_long_phase1_amd.configs import CONFIGS
+from block_sparse_long_phase1_amd.configs import CONFIGS, StarConfig
 from tests._parity import assert_lse, assert_out, flush_print
 
 pytestmark = pytest.mark.gpu
@@ -112,3 +112,40 @@ def test_full_workload(name):
         assert_out(od[t], rod, "%s decode step %d O" % (name, t))
         assert_lse(ld[t], rld, "%s decode step %d LSE" % (name, t))
     flush_print("  decode ok")
+
+
+@pytest.mark.timeout(600)
+def test_phase1_and_query_at_the_token_limit():
+    """The longest context the MFMA kernels take: 2^31 / d tokens per kv head (L = 2^24 at
+    d = 128), where a key's byte offset inside its head reaches 2^32 - 256.  Phase 1 (blocks of
+    4096) and the query phase over four shards, checked on rows at the start and at the very
+    end of the context, where the offsets are largest."""
+    L = 1 << 24
+    cfg = StarConfig("limit", hq=2, hkv=1, d=128, L=L, block=4096, anchor=4096, lq=8, decode_steps=1,
+                     shards=4, dtype="bf16", needle=False, seed=131)
+    flush_print("token limit", L)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    o, lse = sa.star_phase1_encode(q, k, v, cfg.block, cfg.anchor)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lse).all())
+    rows = np.array([0, 1, 4095, 4096, 4097, L // 2 + 77, L - 4096, L - 4095, L - 65, L - 64, L - 2, L - 1],
+                    dtype=np.int64)
+    kh, vh = k.cpu(), v.cpu()
+    ridx = torch.from_numpy(rows).to(DEV)
+    ro, rl = oracle.phase1(q[:, ridx].cpu(), kh, vh, cfg.block, cfg.anchor, rows=rows, q_sampled=True)
+    assert_out(o[:, ridx], ro, "limit phase-1 O")
+    assert_lse(lse[:, ridx], rl, "limit phase-1 LSE")
+    flush_print("  phase1 ok")
+    del o, lse, q
+    p2 = sin.phase2_inputs(cfg, DEV)
+    bounds = cfg.bounds()
+    k_tail = torch.zeros((1, cfg.tail_cap, 128), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :cfg.lq] = p2["k_qry"]
+    v_tail[:, :cfg.lq] = p2["v_qry"]
+    oq, lq_lse = sa.star_phase2_query(p2["q_qry"], k, v, bounds, k_tail, v_tail, cfg.lq)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase2_query(p2["q_qry"].cpu(), kh, vh, bounds, p2["k_qry"].cpu(), p2["v_qry"].cpu())
+    assert_out(oq, ro, "limit query O")
+    assert_lse(lq_lse, rl, "limit query LSE")
+    flush_print("  query ok")
