@@ -15,9 +15,11 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libstarattn.so")
 ARCH = os.environ.get("STAR_OFFLOAD_ARCH", "gfx950")
 
-# Packed fp32 VALU ops stay disabled: the kernels' fp32 math is written as scalar code.
+# Packed fp32 VALU ops stay disabled: the kernels' fp32 math is written as scalar code.  Host
+# symbols are hidden except the C entry points (STAR_API in the header).
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Xarch_host", "-fvisibility=hidden",
                "-I" + INCLUDE, "-I" + CSRC]
 
 

@@ -55,6 +55,10 @@
 extern "C" {
 #endif
 
+/* The entry points below are the library's only exported symbols (it is built with hidden
+ * visibility). */
+#define STAR_API __attribute__((visibility("default")))
+
 typedef enum {
     STAR_OK = 0,
     STAR_ERR_INVALID_ARG = 1,
@@ -66,14 +70,14 @@ typedef enum {
 typedef enum { STAR_F32 = 0, STAR_BF16 = 1 } star_dtype_t;
 
 /* Static name of a status code. */
-const char *star_status_str(star_status_t status);
+STAR_API const char *star_status_str(star_status_t status);
 
 /* Human-readable description of the last failure on the calling thread
  * ("" if none).  The string stays valid until the thread's next call. */
-const char *star_last_error(void);
+STAR_API const char *star_last_error(void);
 
 /* Library version, "major.minor.patch". */
-const char *star_version(void);
+STAR_API const char *star_version(void);
 
 /*
  * Phase 1: anchored blockwise-local context encoding.
@@ -99,7 +103,7 @@ const char *star_version(void);
  * at most 2^31 / d tokens (more returns STAR_ERR_UNSUPPORTED); fp32 and other
  * head dims (d % 4 == 0, d <= 256) run the vector kernel.
  */
-star_status_t star_phase1_encode(const void *q, const void *k, const void *v,
+STAR_API star_status_t star_phase1_encode(const void *q, const void *k, const void *v,
                                  void *o, float *lse,
                                  int64_t L, int64_t block, int64_t anchor,
                                  int32_t hq, int32_t hkv, int32_t d,
@@ -125,9 +129,9 @@ star_status_t star_phase1_encode(const void *q, const void *k, const void *v,
  * 2^31 / d token limit of the MFMA kernel as for star_phase1_encode (n_kv
  * counts the tokens).
  */
-size_t star_phase2_workspace_bytes(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv, int32_t d);
+STAR_API size_t star_phase2_workspace_bytes(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv, int32_t d);
 
-star_status_t star_phase2_partial(const void *q, int32_t rows,
+STAR_API star_status_t star_phase2_partial(const void *q, int32_t rows,
                                   const void *k, const void *v,
                                   int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
                                   int32_t hq, int32_t hkv, int32_t d,
@@ -161,9 +165,9 @@ star_status_t star_phase2_partial(const void *q, int32_t rows,
  * bf16 with d = 64 or 128: two kernel launches (the partials of every key split of
  * every partition, then their merge).  Other shapes: one vector-path launch.
  */
-size_t star_phase2_query_workspace_bytes(int32_t rows, int32_t n_shards, int32_t hq, int32_t hkv, int32_t d);
+STAR_API size_t star_phase2_query_workspace_bytes(int32_t rows, int32_t n_shards, int32_t hq, int32_t hkv, int32_t d);
 
-star_status_t star_phase2_query(const void *q, int32_t rows,
+STAR_API star_status_t star_phase2_query(const void *q, int32_t rows,
                                 const void *k_ctx, const void *v_ctx, int64_t L,
                                 const int64_t *shard_bounds, int32_t n_shards,
                                 const void *k_tail, const void *v_tail, int64_t tail_len, int64_t tail_cap,
@@ -184,7 +188,7 @@ star_status_t star_phase2_query(const void *q, int32_t rows,
  *   partitions are all empty get o = 0 and lse = -inf.
  * One kernel launch.
  */
-star_status_t star_softmax_merge(const float *a, const float *m, const float *l, int32_t n_parts,
+STAR_API star_status_t star_softmax_merge(const float *a, const float *m, const float *l, int32_t n_parts,
                                  int32_t hq, int32_t rows, int32_t d,
                                  void *o, star_dtype_t out_dt, float *lse_out, hipStream_t stream);
 
@@ -217,10 +221,10 @@ star_status_t star_softmax_merge(const float *a, const float *m, const float *l,
  * 8 or 16: that launch without the merge, then a merge launch.  Other shapes:
  * an append launch and a vector-path launch.
  */
-size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards,
+STAR_API size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards,
                                    int32_t hq, int32_t hkv, int32_t d);
 
-star_status_t star_decode_step(const void *q_new, const void *k_new, const void *v_new,
+STAR_API star_status_t star_decode_step(const void *q_new, const void *k_new, const void *v_new,
                                const void *k_ctx, const void *v_ctx, int64_t L,
                                const int64_t *shard_bounds, int32_t n_shards,
                                void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
@@ -257,10 +261,10 @@ star_status_t star_decode_step(const void *q_new, const void *k_new, const void 
  *   out [hkv, tokens, d] uint8 (device, 16-byte aligned), written.
  *   One kernel launch.  x and out may not overlap.
  */
-star_status_t star_kv_fp8_scales(const void *x, int64_t tokens, int32_t hkv, int32_t d,
+STAR_API star_status_t star_kv_fp8_scales(const void *x, int64_t tokens, int32_t hkv, int32_t d,
                                  star_dtype_t dt, float *scale, hipStream_t stream);
 
-star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32_t hkv, int32_t d,
+STAR_API star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32_t hkv, int32_t d,
                                    star_dtype_t dt, const float *scale, void *out,
                                    hipStream_t stream);
 
@@ -278,7 +282,7 @@ star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32_t hkv, i
  *   kernel launches as star_phase2_query's bf16 path; the context tiles are
  *   widened exactly to bf16 on their way into LDS.
  */
-star_status_t star_phase2_query_kv8(const void *q, int32_t rows,
+STAR_API star_status_t star_phase2_query_kv8(const void *q, int32_t rows,
                                     const void *k_ctx8, const void *v_ctx8,
                                     const float *k_scale, const float *v_scale, int64_t L,
                                     const int64_t *shard_bounds, int32_t n_shards,
@@ -301,7 +305,7 @@ star_status_t star_phase2_query_kv8(const void *q, int32_t rows,
  *   STAR_ERR_UNSUPPORTED.  The workspace is star_decode_workspace_bytes(...)
  *   bytes, with the same rules.  Launches as star_decode_step's bf16 path.
  */
-star_status_t star_decode_step_kv8(const void *q_new, const void *k_new, const void *v_new,
+STAR_API star_status_t star_decode_step_kv8(const void *q_new, const void *k_new, const void *v_new,
                                    const void *k_ctx8, const void *v_ctx8,
                                    const float *k_scale, const float *v_scale, int64_t L,
                                    const int64_t *shard_bounds, int32_t n_shards,

@@ -32,6 +32,21 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_exports_nothing_else():
+    """The shared library's exported functions are exactly the header's entry points."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    if not os.path.exists(sa.LIB_PATH):
+        sa_build.build()
+    out = subprocess.run([nm, "-D", "--defined-only", sa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    funcs = sorted(line.split()[-1] for line in out.splitlines() if line.split()[1:2] == ["T"])
+    assert funcs == declared_functions(), funcs
+
+
 def test_status_strings(lib):
     assert lib.star_status_str(0) == b"STAR_OK"
     assert lib.star_status_str(1) == b"STAR_ERR_INVALID_ARG"
