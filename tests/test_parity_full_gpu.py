@@ -119,7 +119,7 @@ def test_phase1_and_query_at_the_token_limit():
     """The longest context the MFMA kernels take: 2^31 / d tokens per kv head (L = 2^24 at
     d = 128), where a key's byte offset inside its head reaches 2^32 - 256.  Phase 1 (blocks of
     4096) and the query phase over four shards, checked on rows at the start and at the very
-    end of the context, where the offsets are largest."""
+    end of the context, where the offsets are largest; then one decode step over it all."""
     L = 1 << 24
     cfg = StarConfig("limit", hq=2, hkv=1, d=128, L=L, block=4096, anchor=4096, lq=8, decode_steps=1,
                      shards=4, dtype="bf16", needle=False, seed=131)
@@ -149,3 +149,12 @@ def test_phase1_and_query_at_the_token_limit():
     assert_out(oq, ro, "limit query O")
     assert_lse(lq_lse, rl, "limit query LSE")
     flush_print("  query ok")
+    # one decode step over the whole context (chunks of about 62K tokens)
+    ws = sa.decode_workspace(L, cfg.tail_cap, len(bounds) - 1, 2, 1, 128, DEV)
+    od, ld = sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds, k_tail, v_tail,
+                                 cfg.lq, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.phase2_decode(p2["q_dec"][0].cpu(), kh, vh, bounds, k_tail.cpu(), v_tail.cpu(), cfg.lq + 1)
+    assert_out(od, ro, "limit decode O")
+    assert_lse(ld, rl, "limit decode LSE")
+    flush_print("  decode ok")
