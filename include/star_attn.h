@@ -104,10 +104,10 @@ STAR_API const char *star_version(void);
  * head dims (d % 4 == 0, d <= 256) run the vector kernel.
  */
 STAR_API star_status_t star_phase1_encode(const void *q, const void *k, const void *v,
-                                 void *o, float *lse,
-                                 int64_t L, int64_t block, int64_t anchor,
-                                 int32_t hq, int32_t hkv, int32_t d,
-                                 star_dtype_t dt, float scale, hipStream_t stream);
+                                          void *o, float *lse,
+                                          int64_t L, int64_t block, int64_t anchor,
+                                          int32_t hq, int32_t hkv, int32_t d,
+                                          star_dtype_t dt, float scale, hipStream_t stream);
 
 /*
  * Phase 2, one partition ("host"): local attention of the query rows over
@@ -132,12 +132,12 @@ STAR_API star_status_t star_phase1_encode(const void *q, const void *k, const vo
 STAR_API size_t star_phase2_workspace_bytes(int32_t rows, int64_t n_kv, int32_t hq, int32_t hkv, int32_t d);
 
 STAR_API star_status_t star_phase2_partial(const void *q, int32_t rows,
-                                  const void *k, const void *v,
-                                  int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
-                                  int32_t hq, int32_t hkv, int32_t d,
-                                  star_dtype_t dt, float scale,
-                                  float *a_out, float *m_out, float *l_out,
-                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                           const void *k, const void *v,
+                                           int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
+                                           int32_t hq, int32_t hkv, int32_t d,
+                                           star_dtype_t dt, float scale,
+                                           float *a_out, float *m_out, float *l_out,
+                                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Phase 2 query encoding on the query host, every partition in one call.
@@ -162,19 +162,21 @@ STAR_API star_status_t star_phase2_partial(const void *q, int32_t rows,
  *   workspace: star_phase2_query_workspace_bytes(rows, n_shards, hq, hkv, d)
  *         bytes (may be 0 for shapes without the MFMA path; then workspace may
  *         be NULL).  Scratch only: its contents need no initialisation.
- * bf16 with d = 64 or 128: two kernel launches (the partials of every key split of
- * every partition, then their merge).  Other shapes: one vector-path launch.
+ * bf16 with d = 64 or 128 and hq/hkv a divisor of 256: two kernel launches (the
+ * partials of every key split of every partition, then their merge), for at most
+ * 2^31 / d tokens in the context and in the query host's cache (more returns
+ * STAR_ERR_UNSUPPORTED).  Other shapes: one vector-path launch.
  */
 STAR_API size_t star_phase2_query_workspace_bytes(int32_t rows, int32_t n_shards, int32_t hq, int32_t hkv, int32_t d);
 
 STAR_API star_status_t star_phase2_query(const void *q, int32_t rows,
-                                const void *k_ctx, const void *v_ctx, int64_t L,
-                                const int64_t *shard_bounds, int32_t n_shards,
-                                const void *k_tail, const void *v_tail, int64_t tail_len, int64_t tail_cap,
-                                int32_t hq, int32_t hkv, int32_t d,
-                                star_dtype_t dt, float scale,
-                                void *o, float *lse,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                         const void *k_ctx, const void *v_ctx, int64_t L,
+                                         const int64_t *shard_bounds, int32_t n_shards,
+                                         const void *k_tail, const void *v_tail, int64_t tail_len, int64_t tail_cap,
+                                         int32_t hq, int32_t hkv, int32_t d,
+                                         star_dtype_t dt, float scale,
+                                         void *o, float *lse,
+                                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Global aggregation of partitions in log space.
@@ -189,8 +191,8 @@ STAR_API star_status_t star_phase2_query(const void *q, int32_t rows,
  * One kernel launch.
  */
 STAR_API star_status_t star_softmax_merge(const float *a, const float *m, const float *l, int32_t n_parts,
-                                 int32_t hq, int32_t rows, int32_t d,
-                                 void *o, star_dtype_t out_dt, float *lse_out, hipStream_t stream);
+                                          int32_t hq, int32_t rows, int32_t d,
+                                          void *o, star_dtype_t out_dt, float *lse_out, hipStream_t stream);
 
 /*
  * Phase 2, one generated token on the query host.
@@ -216,22 +218,22 @@ STAR_API star_status_t star_softmax_merge(const float *a, const float *m, const 
  *         counters back at zero).  Calls that share a workspace must be
  *         ordered on one stream.
  *   0 <= tail_len < tail_cap.
- * bf16 with d = 64 or 128 and hq/hkv <= 4: one kernel launch (chunk partials,
- * the append, and the merge done by the last chunk of each kv head); hq/hkv of
- * 8 or 16: that launch without the merge, then a merge launch.  Other shapes:
- * an append launch and a vector-path launch.
+ * bf16 with d = 64 or 128 and hq/hkv of 1, 2 or 4: one kernel launch (chunk
+ * partials, the append, and the merge done by the last chunk of each kv head);
+ * hq/hkv of 8 or 16: that launch without the merge, then a merge launch.  Other
+ * shapes: an append launch and a vector-path launch.
  */
 STAR_API size_t star_decode_workspace_bytes(int64_t L, int64_t tail_cap, int32_t n_shards,
-                                   int32_t hq, int32_t hkv, int32_t d);
+                                            int32_t hq, int32_t hkv, int32_t d);
 
 STAR_API star_status_t star_decode_step(const void *q_new, const void *k_new, const void *v_new,
-                               const void *k_ctx, const void *v_ctx, int64_t L,
-                               const int64_t *shard_bounds, int32_t n_shards,
-                               void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
-                               int32_t hq, int32_t hkv, int32_t d,
-                               star_dtype_t dt, float scale,
-                               void *o, float *lse,
-                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                        const void *k_ctx, const void *v_ctx, int64_t L,
+                                        const int64_t *shard_bounds, int32_t n_shards,
+                                        void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
+                                        int32_t hq, int32_t hkv, int32_t d,
+                                        star_dtype_t dt, float scale,
+                                        void *o, float *lse,
+                                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * E4M3 context KV cache.
@@ -262,11 +264,11 @@ STAR_API star_status_t star_decode_step(const void *q_new, const void *k_new, co
  *   One kernel launch.  x and out may not overlap.
  */
 STAR_API star_status_t star_kv_fp8_scales(const void *x, int64_t tokens, int32_t hkv, int32_t d,
-                                 star_dtype_t dt, float *scale, hipStream_t stream);
+                                          star_dtype_t dt, float *scale, hipStream_t stream);
 
 STAR_API star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32_t hkv, int32_t d,
-                                   star_dtype_t dt, const float *scale, void *out,
-                                   hipStream_t stream);
+                                            star_dtype_t dt, const float *scale, void *out,
+                                            hipStream_t stream);
 
 /*
  * Phase 2 query encoding over an E4M3 context cache.
@@ -283,15 +285,15 @@ STAR_API star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32
  *   widened exactly to bf16 on their way into LDS.
  */
 STAR_API star_status_t star_phase2_query_kv8(const void *q, int32_t rows,
-                                    const void *k_ctx8, const void *v_ctx8,
-                                    const float *k_scale, const float *v_scale, int64_t L,
-                                    const int64_t *shard_bounds, int32_t n_shards,
-                                    const void *k_tail, const void *v_tail,
-                                    int64_t tail_len, int64_t tail_cap,
-                                    int32_t hq, int32_t hkv, int32_t d,
-                                    star_dtype_t dt, float scale,
-                                    void *o, float *lse,
-                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                             const void *k_ctx8, const void *v_ctx8,
+                                             const float *k_scale, const float *v_scale, int64_t L,
+                                             const int64_t *shard_bounds, int32_t n_shards,
+                                             const void *k_tail, const void *v_tail,
+                                             int64_t tail_len, int64_t tail_cap,
+                                             int32_t hq, int32_t hkv, int32_t d,
+                                             star_dtype_t dt, float scale,
+                                             void *o, float *lse,
+                                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Phase 2, one generated token over an E4M3 context cache.
@@ -306,14 +308,14 @@ STAR_API star_status_t star_phase2_query_kv8(const void *q, int32_t rows,
  *   bytes, with the same rules.  Launches as star_decode_step's bf16 path.
  */
 STAR_API star_status_t star_decode_step_kv8(const void *q_new, const void *k_new, const void *v_new,
-                                   const void *k_ctx8, const void *v_ctx8,
-                                   const float *k_scale, const float *v_scale, int64_t L,
-                                   const int64_t *shard_bounds, int32_t n_shards,
-                                   void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
-                                   int32_t hq, int32_t hkv, int32_t d,
-                                   star_dtype_t dt, float scale,
-                                   void *o, float *lse,
-                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                            const void *k_ctx8, const void *v_ctx8,
+                                            const float *k_scale, const float *v_scale, int64_t L,
+                                            const int64_t *shard_bounds, int32_t n_shards,
+                                            void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
+                                            int32_t hq, int32_t hkv, int32_t d,
+                                            star_dtype_t dt, float scale,
+                                            void *o, float *lse,
+                                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }
