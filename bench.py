@@ -364,7 +364,9 @@ def cpu_baseline(cfg, q, k, v, seconds):
         done += batch
         batch = min(batch * 2, 1024)
     return {"value": done / elapsed, "unit": "context tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d seeded-random Phase-1 context rows x all %d q heads of %s, fp64 C oracle, %.1f s on %s"
+            "sample": "%d seeded-random Phase-1 context rows x all %d q heads of %s, fp64 C oracle, %.1f s on %s; "
+                      "value = rows per second, i.e. the full context's rate extrapolated from the sample "
+                      "(uniformly drawn rows carry the context's mean cost per row)"
                       % (done, cfg.hq, cfg.name, elapsed, cpu_model())}
 
 
