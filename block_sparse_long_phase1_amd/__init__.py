@@ -59,6 +59,9 @@ def load_library(path: str | None = None):
         lib.star_phase2_partial.argtypes = [vp, i32, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int, f32,
                                             vp, vp, vp, vp, sz, vp]
         lib.star_phase2_partial.restype = ctypes.c_int
+        lib.star_phase2_partial_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int,
+                                                f32, vp, vp, vp, vp, sz, vp]
+        lib.star_phase2_partial_kv8.restype = ctypes.c_int
         lib.star_softmax_merge.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, ctypes.c_int, vp, vp]
         lib.star_softmax_merge.restype = ctypes.c_int
         lib.star_phase2_query_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -189,6 +192,16 @@ def _kv_view(t, q, name, hkv, d):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _kv8_view(t, name, hkv, d):
+    """Base pointer of a (possibly strided) uint8 E4M3 partition view [Hkv, n, d]."""
+    torch = _torch()
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda or t.dtype != torch.uint8 or t.shape[0] != hkv or t.shape[-1] != d or t.stride(-1) != 1:
+        raise ValueError("%s must be a device uint8 [Hkv, n, d] view with unit last stride" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def star_phase2_partial(q, k, v, kv_head_stride: int, n_kv: int, causal_offset: int = -1,
                         a_out=None, m_out=None, l_out=None, workspace=None, scale=None, stream=None):
     """Local attention of q [Hq,rows,d] over one KV partition.
@@ -219,6 +232,36 @@ def star_phase2_partial(q, k, v, kv_head_stride: int, n_kv: int, causal_offset: 
         n_kv, causal_offset, hq, hkv, d, _dt(q), _scale(d, scale), _f32(a_out, "a_out", (hq, rows, d)),
         _f32(m_out, "m_out", (hq, rows)), _f32(l_out, "l_out", (hq, rows)), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "star_phase2_partial")
+    return a_out, m_out, l_out
+
+
+def star_phase2_partial_kv8(q, k8, v8, k_scale, v_scale, kv_head_stride: int, n_kv: int, causal_offset: int = -1,
+                            a_out=None, m_out=None, l_out=None, workspace=None, scale=None, stream=None):
+    """star_phase2_partial over a partition of E4M3 codes: k8/v8 are uint8 device views
+    [Hkv, >=n_kv, d] (e.g. ``k8_ctx[:, lo:]``) with fp32 scales [Hkv]; q is bf16."""
+    torch = _torch()
+    hq, rows, d = q.shape
+    hkv = k8.shape[0]
+    dev = q.device
+    if a_out is None:
+        a_out = torch.empty((hq, rows, d), dtype=torch.float32, device=dev)
+    if m_out is None:
+        m_out = torch.empty((hq, rows), dtype=torch.float32, device=dev)
+    if l_out is None:
+        l_out = torch.empty((hq, rows), dtype=torch.float32, device=dev)
+    if n_kv > 0 and k8.shape[1] < n_kv:
+        raise ValueError("k8 view holds %d tokens, n_kv is %d" % (k8.shape[1], n_kv))
+    need = star_phase2_workspace_bytes(rows, n_kv, hq, hkv, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().star_phase2_partial_kv8(
+        _dev(q, "q"), rows, _kv8_view(k8, "k8", hkv, d), _kv8_view(v8, "v8", hkv, d),
+        _f32(k_scale, "k_scale", (hkv,)), _f32(v_scale, "v_scale", (hkv,)), kv_head_stride, n_kv, causal_offset,
+        hq, hkv, d, _dt(q), _scale(d, scale), _f32(a_out, "a_out", (hq, rows, d)), _f32(m_out, "m_out", (hq, rows)),
+        _f32(l_out, "l_out", (hq, rows)), ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "star_phase2_partial_kv8")
     return a_out, m_out, l_out
 
 
@@ -398,4 +441,5 @@ __all__ = [
     "star_phase2_query_workspace_bytes", "star_phase2_query",
     "star_decode_workspace_bytes", "star_decode_step", "decode_workspace", "STAR_F32", "STAR_BF16",
     "star_kv_fp8_scales", "star_kv_quantize_fp8", "star_decode_step_kv8", "star_phase2_query_kv8",
+    "star_phase2_partial_kv8",
 ]

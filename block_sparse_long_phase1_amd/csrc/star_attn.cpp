@@ -111,6 +111,48 @@ star_status_t check_query(const void* q, int32_t rows, int64_t L, const int64_t*
     return STAR_OK;
 }
 
+// One partition on the MFMA kernel (E4M3 codes when k_scale is set): its key splits, then
+// their merge into (A, m, l) when there are several.
+star_status_t partial_mfma(const void* q, int32_t rows, const void* k, const void* v, const float* k_scale,
+                           const float* v_scale, int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
+                           int32_t hq, int32_t hkv, int32_t d, float scale, float* a_out, float* m_out,
+                           float* l_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           const char* who) {
+    if (n_kv > star::attn_mfma_max_tokens(d))
+        return fail(STAR_ERR_UNSUPPORTED, "n_kv (%lld) above %lld tokens per partition", (long long)n_kv,
+                    (long long)star::attn_mfma_max_tokens(d));
+    star::PartPlan plan = {};
+    plan.n_parts = 1;
+    plan.k[0] = k;
+    plan.v[0] = v;
+    plan.head_stride[0] = kv_head_stride;
+    plan.n_kv[0] = n_kv;
+    plan.causal[0] = causal_offset < 0 ? -1 : causal_offset;
+    plan.n_f8 = k_scale ? 1 : 0;
+    plan.k_scale = k_scale;
+    plan.v_scale = v_scale;
+    const int nrt = star::partial_mfma_plan(plan, rows, hq, hkv);
+    const int32_t ns = plan.split_prefix[1];
+    const uint16_t* qb = static_cast<const uint16_t*>(q);
+    hipError_t e;
+    if (ns == 1) {
+        e = star::launch_partial_mfma(qb, rows, hq, hkv, d, scale, plan, nrt, a_out, m_out, l_out, stream);
+        if (e != hipSuccess) return hip_fail(e, who);
+        return ok();
+    }
+    const size_t need = partials_bytes(ns, (int64_t)hq * rows, d);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    float *wa, *wm, *wl;
+    partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
+    e = star::launch_partial_mfma(qb, rows, hq, hkv, d, scale, plan, nrt, wa, wm, wl, stream);
+    if (e != hipSuccess) return hip_fail(e, who);
+    e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, a_out, false, nullptr, m_out, l_out, stream);
+    if (e != hipSuccess) return hip_fail(e, who);
+    return ok();
+}
+
 // The query phase on the MFMA kernel: one partial launch over every context shard and the
 // query host's cache (E4M3 context shards when k_scale is set), then the merge.
 star_status_t query_mfma(const void* q, int32_t rows, const void* k_ctx, const void* v_ctx, const float* k_scale,
@@ -296,51 +338,53 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
             (reinterpret_cast<uintptr_t>(m_out) & 3u) || (reinterpret_cast<uintptr_t>(l_out) & 3u) ||
             ((kv_head_stride * elem_bytes(dt)) % 16))
             return fail(STAR_ERR_INVALID_ARG, "pointers and the kv head stride must be 16-byte aligned");
-        hipError_t e;
-        if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv)) {
-            if (n_kv > star::attn_mfma_max_tokens(d))
-                return fail(STAR_ERR_UNSUPPORTED, "n_kv (%lld) above %lld tokens per partition", (long long)n_kv,
-                            (long long)star::attn_mfma_max_tokens(d));
-            star::PartPlan plan = {};
-            plan.n_parts = 1;
-            plan.k[0] = static_cast<const uint16_t*>(k);
-            plan.v[0] = static_cast<const uint16_t*>(v);
-            plan.head_stride[0] = kv_head_stride;
-            plan.n_kv[0] = n_kv;
-            plan.causal[0] = causal_offset < 0 ? -1 : causal_offset;
-            const int nrt = star::partial_mfma_plan(plan, rows, hq, hkv);
-            const int32_t ns = plan.split_prefix[1];
-            if (ns == 1) {
-                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, d, scale, plan, nrt,
-                                              a_out, m_out, l_out, stream);
-                if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
-            } else {
-                size_t need = partials_bytes(ns, (int64_t)hq * rows, d);
-                if (!workspace || workspace_bytes < need || !aligned16(workspace))
-                    return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
-                                need, workspace ? workspace_bytes : (size_t)0);
-                float *wa, *wm, *wl;
-                partials_ptrs(workspace, ns, (int64_t)hq * rows, d, &wa, &wm, &wl);
-                e = star::launch_partial_mfma(static_cast<const uint16_t*>(q), rows, hq, hkv, d, scale, plan, nrt,
-                                              wa, wm, wl, stream);
-                if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
-                e = star::launch_merge(wa, wm, wl, ns, (int64_t)hq * rows, d, a_out, false, nullptr, m_out, l_out, stream);
-                if (e != hipSuccess) return hip_fail(e, "star_phase2_partial merge launch");
-            }
-        } else {
-            star::RowAttnArgs a = {};
-            a.q = q; a.q_rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
-            a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 1;
-            a.n_seg = n_kv > 0 ? 1 : 0;
-            a.seg[0].k = k; a.seg[0].v = v; a.seg[0].head_stride = kv_head_stride;
-            a.seg[0].n = n_kv; a.seg[0].causal_lim = causal_offset;
-            a.a_out = a_out; a.m_out = m_out; a.l_out = l_out;
-            e = star::launch_row_attn(a, rows, stream);
-            if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
-        }
+        if (dt == STAR_BF16 && star::attn_mfma_supported(d, hq, hkv))
+            return partial_mfma(q, rows, k, v, nullptr, nullptr, kv_head_stride, n_kv, causal_offset, hq, hkv, d,
+                                scale, a_out, m_out, l_out, workspace, workspace_bytes, stream, "star_phase2_partial");
+        star::RowAttnArgs a = {};
+        a.q = q; a.q_rows = rows; a.hq = hq; a.hkv = hkv; a.d = d;
+        a.is_bf16 = dt == STAR_BF16; a.scale = scale; a.mode = 1;
+        a.n_seg = n_kv > 0 ? 1 : 0;
+        a.seg[0].k = k; a.seg[0].v = v; a.seg[0].head_stride = kv_head_stride;
+        a.seg[0].n = n_kv; a.seg[0].causal_lim = causal_offset;
+        a.a_out = a_out; a.m_out = m_out; a.l_out = l_out;
+        const hipError_t e = star::launch_row_attn(a, rows, stream);
+        if (e != hipSuccess) return hip_fail(e, "star_phase2_partial launch");
         return ok();
     } catch (...) {
         return fail(STAR_ERR_HIP, "star_phase2_partial: internal error");
+    }
+}
+
+star_status_t star_phase2_partial_kv8(const void* q, int32_t rows, const void* k8, const void* v8,
+                                      const float* k_scale, const float* v_scale, int64_t kv_head_stride,
+                                      int64_t n_kv, int64_t causal_offset, int32_t hq, int32_t hkv, int32_t d,
+                                      star_dtype_t dt, float scale, float* a_out, float* m_out, float* l_out,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    try {
+        if (!q || !a_out || !m_out || !l_out || !k_scale || !v_scale)
+            return fail(STAR_ERR_INVALID_ARG, "q, the scales, a_out, m_out, l_out must be non-null");
+        if (n_kv > 0 && (!k8 || !v8)) return fail(STAR_ERR_INVALID_ARG, "k8 and v8 must be non-null when n_kv > 0");
+        if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
+        if (n_kv < 0) return fail(STAR_ERR_INVALID_ARG, "n_kv must be >= 0");
+        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        star_status_t s = check_heads(hq, hkv, d, dt);
+        if (s != STAR_OK) return s;
+        if (kv_head_stride < 0) return fail(STAR_ERR_INVALID_ARG, "kv_head_stride must be >= 0");
+        if (hkv > 1 && kv_head_stride < n_kv * d)
+            return fail(STAR_ERR_INVALID_ARG, "kv_head_stride (%lld) smaller than n_kv * d", (long long)kv_head_stride);
+        if (!aligned16(q) || (k8 && !aligned16(k8)) || (v8 && !aligned16(v8)) || !aligned16(a_out) ||
+            (reinterpret_cast<uintptr_t>(m_out) & 3u) || (reinterpret_cast<uintptr_t>(l_out) & 3u) ||
+            (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u) ||
+            (kv_head_stride % 16))
+            return fail(STAR_ERR_INVALID_ARG,
+                        "pointers and the kv head stride must be 16-byte aligned (scales, m and l 4-byte)");
+        if (dt != STAR_BF16 || !star::attn_mfma_supported(d, hq, hkv))
+            return fail(STAR_ERR_UNSUPPORTED, "E4M3 partial needs bf16, d = 64 or 128 and hq/hkv dividing 256");
+        return partial_mfma(q, rows, k8, v8, k_scale, v_scale, kv_head_stride, n_kv, causal_offset, hq, hkv, d,
+                            scale, a_out, m_out, l_out, workspace, workspace_bytes, stream, "star_phase2_partial_kv8");
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_phase2_partial_kv8: internal error");
     }
 }
 

@@ -271,6 +271,29 @@ STAR_API star_status_t star_kv_quantize_fp8(const void *x, int64_t tokens, int32
                                             hipStream_t stream);
 
 /*
+ * Phase 2, one partition held as E4M3 codes.
+ * [SUM] 3.4 Phase 2 Step 3 over the dequantised partition (see above).
+ *
+ * Arguments and behaviour as star_phase2_partial, except:
+ *   k8, v8: E4M3 codes (uint8, 16-byte aligned) replace k / v, with the same
+ *   element offsets (g * kv_head_stride + t * d; kv_head_stride a multiple of
+ *   16); k_scale, v_scale [hkv] fp32 (device, 4-byte aligned) are their
+ *   scales, so token t of kv head g has key k_scale[g] * decode(k8[...]).
+ *   The (A, m, l) outputs are those of the dequantised partition.  dt must be
+ *   STAR_BF16 (q), d 64 or 128 and hq/hkv a divisor of 256; other shapes return
+ *   STAR_ERR_UNSUPPORTED.  The workspace is star_phase2_workspace_bytes(...)
+ *   bytes, with the same rules.
+ */
+STAR_API star_status_t star_phase2_partial_kv8(const void *q, int32_t rows,
+                                               const void *k8, const void *v8,
+                                               const float *k_scale, const float *v_scale,
+                                               int64_t kv_head_stride, int64_t n_kv, int64_t causal_offset,
+                                               int32_t hq, int32_t hkv, int32_t d,
+                                               star_dtype_t dt, float scale,
+                                               float *a_out, float *m_out, float *l_out,
+                                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Phase 2 query encoding over an E4M3 context cache.
  * [SUM] 3.4 Phase 2 Steps 1-5 over the dequantised context (see above).
  *

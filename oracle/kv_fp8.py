@@ -103,6 +103,14 @@ def _dequantized_cache(k8, v8, k_scale, v_scale):
     return kd, vd
 
 
+def partial_kv8(q, k8, v8, k_scale, v_scale, lo, hi, causal_offset=-1, scale=None, threads=None):
+    """The local (A, m, l) of q [Hq, rows, d] over tokens [lo, hi) of an E4M3 cache k8/v8
+    [Hkv, T, d] with per-kv-head scales: the plain partial (section 3.4, Phase 2 Step 3) over
+    the dequantised values, with the same optional causal offset."""
+    kd, vd = _dequantized_cache(k8, v8, k_scale, v_scale)
+    return partial(np.ascontiguousarray(widen(q)), kd, vd, int(lo), int(hi), int(causal_offset), scale, threads)
+
+
 def phase2_decode_kv8(q_t, k8, v8, k_scale, v_scale, shard_bounds, k_tail, v_tail, tail_len,
                       scale=None, threads=None):
     """One generated token over an E4M3 context cache: q_t [Hq, d] attends to every context

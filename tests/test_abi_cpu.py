@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -144,6 +144,25 @@ def test_decode_kv8_validation(lib):
     assert d(*args(dim=96)) == 2                           # head dim 96
     assert d(*args(hq=6, hkv=2)) == 2                      # G = 3
     assert d(*args(ws=16)) == 4                            # workspace too small
+
+
+def test_partial_kv8_validation(lib):
+    p = lib.star_phase2_partial_kv8
+
+    def args(q=FAKE, ks=FAKE, k8=FAKE, stride=1024 * 128, n_kv=1024, hq=4, hkv=2, dim=128, dt=1, rows=8, ws=1 << 30):
+        return (q, rows, k8, FAKE, ks, FAKE, stride, n_kv, -1, hq, hkv, dim, dt, 0.1, FAKE, FAKE, FAKE, FAKE, ws, NULL)
+    assert p(*args(q=NULL)) == 1                           # null q
+    assert p(*args(ks=NULL)) == 1                          # null scale
+    assert p(*args(k8=NULL)) == 1                          # null codes with tokens
+    assert p(*args(k8=ctypes.c_void_p(0x100008))) == 1     # misaligned codes
+    assert p(*args(stride=1024 * 128 + 8)) == 1            # stride not a multiple of 16 bytes
+    assert p(*args(stride=100)) == 1                       # stride < n_kv * d
+    assert p(*args(rows=0)) == 1                           # no rows
+    assert p(*args(dt=0)) == 2                             # fp32: no E4M3 path
+    assert p(*args(dim=96)) == 2                           # head dim 96
+    assert p(*args(hq=6, hkv=2)) == 2                      # G = 3
+    assert p(*args(n_kv=(1 << 24) + 1, stride=((1 << 24) + 1) * 128)) == 2   # past the 32-bit offsets
+    assert p(*args(n_kv=1 << 20, stride=(1 << 20) * 128, ws=16)) == 4         # split partition, short workspace
 
 
 def test_query_kv8_validation(lib):

@@ -205,3 +205,53 @@ def test_kv8_query_rows_after_cached_tokens_against_dense_softmax():
             w = np.exp(x - x.max())
             np.testing.assert_allclose(o8[h, i], w @ vals / w.sum(), rtol=0, atol=1e-12)
             np.testing.assert_allclose(l8[h, i], x.max() + np.log(w.sum()), rtol=1e-13)
+
+
+@pytest.mark.parametrize("off", [-1, 3])
+def test_kv8_partial_equals_plain_oracle_on_fp32_exact_values(off):
+    """Power-of-two scales: the E4M3 partial over tokens [lo, hi) equals the plain partial on
+    the exact dequantised values, with and without a causal offset; swapping the heads' K
+    scales changes it."""
+    rng = np.random.default_rng(29)
+    hq, hkv, T, d, rows, lo, hi = 4, 2, 150, 32, 6, 20, 140
+    k8 = rng.integers(0, 256, (hkv, T, d)).astype(np.uint8)
+    v8 = rng.integers(0, 256, (hkv, T, d)).astype(np.uint8)
+    for c in (k8, v8):
+        c[(c & 0x7F) == 0x7F] ^= 1
+    ks = np.float32([2.0 ** -6, 2.0 ** -2])
+    vs = np.float32([2.0 ** 1, 2.0 ** -3])
+    q = rng.standard_normal((hq, rows, d)).astype(np.float32)
+    a8, m8, l8 = f8.partial_kv8(q, k8, v8, ks, vs, lo, hi, off)
+    kd = f8.kv_dequantize(k8, ks).astype(np.float32)
+    vd = f8.kv_dequantize(v8, vs).astype(np.float32)
+    a, m, l = oracle.partial(q, kd, vd, lo, hi, off)
+    np.testing.assert_allclose(a8, a, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m8, m, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(l8, l, rtol=1e-13, atol=0)
+    a_sw, _, _ = f8.partial_kv8(q, k8, v8, ks[::-1].copy(), vs, lo, hi, off)
+    assert np.abs(a_sw - a).max() > 1e-3
+
+
+def test_kv8_partial_against_brute_force():
+    """Tiny case, one row at a time: A is the softmax-weighted mean of the dequantised values
+    over the visible tokens, m their largest scaled score and l the sum of exp(score - m)."""
+    rng = np.random.default_rng(31)
+    hq, hkv, T, d, rows, lo, hi, off = 4, 2, 25, 16, 3, 5, 21, 7
+    k8 = rng.integers(0, 0x7E, (hkv, T, d)).astype(np.uint8) | (rng.integers(0, 2, (hkv, T, d)) << 7).astype(np.uint8)
+    v8 = rng.integers(0, 0x7E, (hkv, T, d)).astype(np.uint8)
+    ks, vs = np.float32([0.02, 0.007]), np.float32([0.05, 0.3])
+    q = rng.standard_normal((hq, rows, d)).astype(np.float32)
+    a8, m8, l8 = f8.partial_kv8(q, k8, v8, ks, vs, lo, hi, off)
+    sc = 1 / np.sqrt(d)
+    G = hq // hkv
+    for h in range(hq):
+        g = h // G
+        for i in range(rows):
+            toks = [t for t in range(lo, hi) if t - lo <= off + i]
+            keys = float(ks[g]) * f8.e4m3_decode(k8[g, toks])
+            vals = float(vs[g]) * f8.e4m3_decode(v8[g, toks])
+            x = sc * keys @ q[h, i].astype(np.float64)
+            w = np.exp(x - x.max())
+            np.testing.assert_allclose(a8[h, i], w @ vals / w.sum(), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(m8[h, i], x.max(), rtol=1e-13)
+            np.testing.assert_allclose(l8[h, i], w.sum(), rtol=1e-13)

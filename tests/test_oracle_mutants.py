@@ -94,6 +94,8 @@ FP8_MUTANTS = {
                               "parts.append(partial(q3, kt, vt, 0, int(tail_len), -1, scale, threads))"),
     "query_tail_offset_off_by_one": ("int(tail_len) - rows, scale, threads))",
                                      "int(tail_len) - rows - 1, scale, threads))"),
+    "partial_ignores_causal_offset": ("int(lo), int(hi), int(causal_offset), scale, threads)",
+                                      "int(lo), int(hi), -1, scale, threads)"),
     "quantize_multiplies": ("qv = (v / s).astype(np.float32)", "qv = (v * s).astype(np.float32)"),
     "absmax_over_256": ("s = (amax.astype(np.float32) / np.float32(E4M3_MAX))",
                         "s = (amax.astype(np.float32) / np.float32(256.0))"),
@@ -109,7 +111,9 @@ def _fp8_pin_calls():
                 p8.test_kv8_decode_equals_plain_oracle_on_fp32_exact_values,
                 lambda: p8.test_kv8_decode_against_dense_softmax(None),
                 p8.test_kv8_query_equals_plain_oracle_on_fp32_exact_values,
-                p8.test_kv8_query_rows_after_cached_tokens_against_dense_softmax]
+                p8.test_kv8_query_rows_after_cached_tokens_against_dense_softmax,
+                lambda: p8.test_kv8_partial_equals_plain_oracle_on_fp32_exact_values(3),
+                p8.test_kv8_partial_against_brute_force]
 
 
 def test_fp8_pins_pass_on_the_real_module():

@@ -164,6 +164,33 @@ def test_query_kv8(hq, hkv, L, bounds, rows, tail_len, tail_cap, d):
     assert_lse(lse, rl, "kv8 query LSE")
 
 
+@pytest.mark.parametrize("hq,hkv,T,lo,hi,rows,off,d", [
+    (8, 2, 3000, 0, 3000, 40, -1, 128),          # the whole cache, no mask
+    (16, 1, 2333, 700, 2333, 9, -1, 64),         # a shard view of a bigger cache, d = 64, G = 16
+    (4, 2, 600, 100, 420, 70, 250, 128),         # causal offset: row i sees partition tokens <= 250 + i
+    (8, 2, 20000, 2000, 20000, 16, -1, 128),     # several key splits, merged into one partial
+    (4, 4, 300, 150, 150, 5, -1, 128),           # an empty partition
+])
+def test_partial_kv8(hq, hkv, T, lo, hi, rows, off, d):
+    """One partition of oracle-made E4M3 codes against the oracle's partial over the
+    dequantised values: A, the log-sum-exp m + log l, and m itself."""
+    flush_print("partial kv8", hq, hkv, T, lo, hi, rows, off, d)
+    cfg = _cfg(hq, hkv, T, T, d=d, seed=101)
+    q = sin.randn(cfg, "q_qry", (hq, rows, d), DEV)
+    k = sin.randn(cfg, "k_ctx", (hkv, T, d), DEV)
+    v = sin.randn(cfg, "v_ctx", (hkv, T, d), DEV)
+    k8, v8, ks, vs, (hk8, hv8, hks, hvs) = _oracle_cache(k, v)
+    a, m, l = sa.star_phase2_partial_kv8(q, k8[:, lo:], v8[:, lo:], ks, vs, T * d, hi - lo, off)
+    torch.cuda.synchronize()
+    if hi == lo:
+        assert torch.all(a == 0) and torch.all(torch.isneginf(m)) and torch.all(l == 0)
+        return
+    ra, rm, rl = of8.partial_kv8(q.cpu(), hk8, hv8, hks, hvs, lo, hi, off)
+    assert_out(a, ra, "kv8 partial A")
+    assert_lse(m + torch.log(l), rm + np.log(rl), "kv8 partial LSE")
+    assert_lse(m, rm, "kv8 partial m")
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_query_kv8_equals_bf16_query_on_representable_values(d):
     """With unit scales and a context whose bf16 values are E4M3 values, the E4M3 query phase
