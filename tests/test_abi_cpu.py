@@ -219,3 +219,22 @@ def test_binding_names_match_abi():
         if n in ("star_status_str", "star_last_error", "star_version"):
             continue
         assert hasattr(sa, n), n
+
+
+def test_missing_library_raises(tmp_path):
+    """Without the native library the binding raises; it has no other implementation."""
+    with pytest.raises(RuntimeError, match="not found"):
+        sa.load_library(str(tmp_path / "libstarattn.so"))
+
+
+def test_host_tensors_are_rejected(lib):
+    """No CPU fallback: host tensors are refused before any native call."""
+    import torch
+    q = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        sa.star_phase1_encode(q, k, k.clone(), 8, 8)
+    with pytest.raises(ValueError, match="device tensor"):
+        sa.star_phase2_query(q, k, k.clone(), [0, 8], k.clone(), k.clone(), 8)
+    with pytest.raises(ValueError, match="device tensor"):
+        sa.star_phase2_partial(q, k, k.clone(), 8 * 128, 8)
