@@ -39,3 +39,14 @@ def test_config_work_counts():
     assert c.decode_step_bytes(0) == 2 * 8 * (32768 + 128 + 1) * 128 * 2
     assert CONFIGS["8b_1m"].n_blocks == 16 and CONFIGS["70b_128k"].n_blocks == 8
     assert CONFIGS["70b_128k"].G == 8
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with a message before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
