@@ -74,6 +74,9 @@ def load_library(path: str | None = None):
         lib.star_decode_step.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32, i32,
                                          ctypes.c_int, f32, vp, vp, vp, sz, vp]
         lib.star_decode_step.restype = ctypes.c_int
+        lib.star_decode_step_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32,
+                                                 i32, ctypes.c_int, f32, vp, vp, vp]
+        lib.star_decode_step_noalloc.restype = ctypes.c_int
         lib.star_kv_fp8_scales.argtypes = [vp, i64, i32, i32, ctypes.c_int, vp, vp]
         lib.star_kv_fp8_scales.restype = ctypes.c_int
         lib.star_kv_quantize_fp8.argtypes = [vp, i64, i32, i32, ctypes.c_int, vp, vp, vp]
@@ -353,6 +356,26 @@ def star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, 
     return o, lse
 
 
+def star_decode_step_noalloc(q_new, k_new, v_new, k_ctx, v_ctx, bounds, k_tail, v_tail, tail_len: int,
+                             o, lse=None, scale=None, stream=None):
+    """star_decode_step without a workspace: the library keeps the chunk partials in its own
+    static device scratch (calls on one GPU must not overlap).  The caller passes the
+    outputs o [Hq,d] (and optionally lse [Hq]); nothing is allocated here either."""
+    hq, d = q_new.shape
+    hkv, L, _ = k_ctx.shape
+    tail_cap = k_tail.shape[1]
+    n_shards = len(bounds) - 1
+    b = (ctypes.c_int64 * (n_shards + 1))(*[int(x) for x in bounds])
+    st = load_library().star_decode_step_noalloc(
+        _dev(q_new, "q_new"), _same(k_new, q_new, "k_new", (hkv, d)), _same(v_new, q_new, "v_new", (hkv, d)),
+        _same(k_ctx, q_new, "k_ctx", (hkv, L, d)), _same(v_ctx, q_new, "v_ctx", (hkv, L, d)), L, b, n_shards,
+        _same(k_tail, q_new, "k_tail", (hkv, tail_cap, d)), _same(v_tail, q_new, "v_tail", (hkv, tail_cap, d)),
+        tail_len, tail_cap, hq, hkv, d, _dt(q_new), _scale(d, scale), _same(o, q_new, "o", (hq, d)),
+        ctypes.c_void_p(0) if lse is None else _f32(lse, "lse", (hq,)), _stream(stream))
+    _check(st, "star_decode_step_noalloc")
+    return o, lse
+
+
 def star_kv_fp8_scales(x, scale=None, stream=None):
     """Per-kv-head E4M3 scales of a context cache x [Hkv, tokens, d] (bf16 or fp32):
     max |x[g]| / 448 (1 for an all-zero head), fp32 [Hkv]."""
@@ -441,5 +464,5 @@ __all__ = [
     "star_phase2_query_workspace_bytes", "star_phase2_query",
     "star_decode_workspace_bytes", "star_decode_step", "decode_workspace", "STAR_F32", "STAR_BF16",
     "star_kv_fp8_scales", "star_kv_quantize_fp8", "star_decode_step_kv8", "star_phase2_query_kv8",
-    "star_phase2_partial_kv8",
+    "star_phase2_partial_kv8", "star_decode_step_noalloc",
 ]

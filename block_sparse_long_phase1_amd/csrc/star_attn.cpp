@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -206,9 +207,11 @@ struct DecodeLaunch {
     unsigned* tickets;
 };
 
+// Workspace layout: the chunk partials, then hkv 32-bit counters.  With `tickets` given, the
+// counters live there instead and the workspace holds the partials only.
 star_status_t plan_decode(const int64_t* shard_bounds, int32_t n_shards, int64_t tail_len, int64_t tail_cap,
                           int32_t hq, int32_t hkv, int32_t d, void* workspace, size_t workspace_bytes,
-                          DecodeLaunch* dl) {
+                          DecodeLaunch* dl, unsigned* tickets = nullptr) {
     star::DecodeChunkPlan& plan = dl->plan;
     plan = {};
     plan.n_shards = n_shards;
@@ -227,12 +230,46 @@ star_status_t plan_decode(const int64_t* shard_bounds, int32_t n_shards, int64_t
     const int64_t n_max = star::decode_max_chunks(tail_cap, n_shards, hkv);
     if (nc > n_max) return fail(STAR_ERR_HIP, "decode chunk plan exceeds its bound");
     const size_t part_bytes = partials_bytes(n_max, hq, d);
-    const size_t need = part_bytes + round_up((size_t)hkv * 4);
+    const size_t need = part_bytes + (tickets ? 0 : round_up((size_t)hkv * 4));
     if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
     partials_ptrs(workspace, n_max, hq, d, &dl->a, &dl->m, &dl->l);
-    dl->tickets = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + part_bytes);
+    dl->tickets = tickets ? tickets : reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + part_bytes);
+    return STAR_OK;
+}
+
+// ---- Scratch of star_decode_step_noalloc, for callers that cannot allocate.
+// A file-scope device array: every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  Its first kNoAllocTicketBytes hold the per-kv-head
+// completion counters, at a fixed place so that no call's partials ever land on them: they
+// are zero when the library is loaded and every completed decode call leaves them at zero.
+// The rest holds one call's chunk partials, which need no initialisation.
+constexpr size_t kNoAllocScratchBytes = STAR_DECODE_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kNoAllocTicketBytes = 4 * STAR_DECODE_NOALLOC_MAX_HKV;
+static_assert(kNoAllocTicketBytes % 256 == 0, "partials stay 256-byte aligned");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The device address of this device's `scratch`, looked up once per device with that device
+// current.  Host code uses this address, never the array's name (a host-side stand-in).
+star_status_t noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "star_decode_step_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(STAR_ERR_UNSUPPORTED, "device ordinal %d above %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "star_decode_step_noalloc: hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(STAR_ERR_HIP, "star_decode_step_noalloc: no device address for the scratch array");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return STAR_OK;
 }
 
@@ -525,6 +562,53 @@ star_status_t star_decode_step(const void* q_new, const void* k_new, const void*
         return ok();
     } catch (...) {
         return fail(STAR_ERR_HIP, "star_decode_step: internal error");
+    }
+}
+
+star_status_t star_decode_step_noalloc(const void* q_new, const void* k_new, const void* v_new,
+                                       const void* k_ctx, const void* v_ctx, int64_t L,
+                                       const int64_t* shard_bounds, int32_t n_shards,
+                                       void* k_tail, void* v_tail, int64_t tail_len, int64_t tail_cap,
+                                       int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt, float scale,
+                                       void* o, float* lse, hipStream_t stream) {
+    try {
+        if (!k_ctx || !v_ctx) return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
+        if (!aligned16(k_ctx) || !aligned16(v_ctx)) return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+        star_status_t s = check_decode(q_new, k_new, v_new, L, shard_bounds, n_shards, k_tail, v_tail, tail_len,
+                                       tail_cap, hq, hkv, d, dt, scale, o, lse);
+        if (s != STAR_OK) return s;
+        if (!(dt == STAR_BF16 && star::decode_bf16_supported(d, hq, hkv))) {
+            // The vector path uses no scratch: the same launches as star_decode_step.
+            return star_decode_step(q_new, k_new, v_new, k_ctx, v_ctx, L, shard_bounds, n_shards, k_tail, v_tail,
+                                    tail_len, tail_cap, hq, hkv, d, dt, scale, o, lse, nullptr, 0, stream);
+        }
+        if (hkv > STAR_DECODE_NOALLOC_MAX_HKV)
+            return fail(STAR_ERR_WORKSPACE, "star_decode_step_noalloc: hkv (%d) above %d", hkv,
+                        STAR_DECODE_NOALLOC_MAX_HKV);
+        const size_t need = partials_bytes(star::decode_max_chunks(tail_cap, n_shards, hkv), hq, d);
+        if (need > kNoAllocScratchBytes - kNoAllocTicketBytes)
+            return fail(STAR_ERR_WORKSPACE,
+                        "star_decode_step_noalloc: this shape needs %zu bytes of chunk partials, above the %zu the "
+                        "static scratch holds; use star_decode_step with a workspace",
+                        need, kNoAllocScratchBytes - kNoAllocTicketBytes);
+        void* base = nullptr;
+        s = noalloc_scratch(&base);
+        if (s != STAR_OK) return s;
+        DecodeLaunch dl;
+        s = plan_decode(shard_bounds, n_shards, tail_len, tail_cap, hq, hkv, d,
+                        static_cast<char*>(base) + kNoAllocTicketBytes, kNoAllocScratchBytes - kNoAllocTicketBytes,
+                        &dl, static_cast<unsigned*>(base));
+        if (s != STAR_OK) return s;
+        const hipError_t e = star::launch_decode_bf16(
+            static_cast<const uint16_t*>(q_new), static_cast<const uint16_t*>(k_new),
+            static_cast<const uint16_t*>(v_new), static_cast<const uint16_t*>(k_ctx),
+            static_cast<const uint16_t*>(v_ctx), nullptr, nullptr, nullptr, nullptr, L,
+            static_cast<uint16_t*>(k_tail), static_cast<uint16_t*>(v_tail), tail_len, tail_cap, hq, hkv, d, scale,
+            dl.plan, dl.a, dl.m, dl.l, dl.tickets, static_cast<uint16_t*>(o), lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "star_decode_step_noalloc launch");
+        return ok();
+    } catch (...) {
+        return fail(STAR_ERR_HIP, "star_decode_step_noalloc: internal error");
     }
 }
 

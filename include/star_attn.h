@@ -33,6 +33,8 @@
  *   frees device memory and keeps no state between calls other than what a
  *   caller-provided workspace holds; entry points that need scratch take such
  *   a workspace, whose size the matching *_workspace_bytes() call returns.
+ *   The one exception, star_decode_step_noalloc, keeps its scratch in a fixed
+ *   static device array instead (see there).
  * Streams and errors.  Every call only enqueues work on `stream` and returns
  *   without synchronising.  Arguments are checked on the host before anything
  *   is enqueued: a bad argument returns STAR_ERR_INVALID_ARG, a shape the
@@ -234,6 +236,38 @@ STAR_API star_status_t star_decode_step(const void *q_new, const void *k_new, co
                                         star_dtype_t dt, float scale,
                                         void *o, float *lse,
                                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * star_decode_step without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.
+ *
+ * Arguments, results and launches as star_decode_step, minus the workspace.
+ * The bf16 MFMA path (d = 64 or 128, hq/hkv of 1, 2, 4, 8 or 16) keeps its
+ * chunk partials and per-kv-head completion counters in a static device array
+ * of STAR_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; the other shapes need no scratch.  A shape
+ * whose partials need more than STAR_DECODE_NOALLOC_SCRATCH_BYTES minus
+ * 4 * STAR_DECODE_NOALLOC_MAX_HKV bytes (the bound star_decode_workspace_bytes
+ * gives, less the counters), or with hkv above STAR_DECODE_NOALLOC_MAX_HKV,
+ * returns STAR_ERR_WORKSPACE before anything is enqueued.  This call never
+ * allocates or frees memory; its first call on a device looks up that device's
+ * copy of the array (no allocation, no stream work).
+ * The counters are zero when the library is loaded and every completed call
+ * leaves them at zero.  All calls on one GPU share its one array: calls that
+ * may overlap on one GPU (on different streams, or from several threads
+ * without ordering) race and give wrong results; order them on one stream.
+ */
+#define STAR_DECODE_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define STAR_DECODE_NOALLOC_MAX_HKV 1024
+
+STAR_API star_status_t star_decode_step_noalloc(const void *q_new, const void *k_new, const void *v_new,
+                                                const void *k_ctx, const void *v_ctx, int64_t L,
+                                                const int64_t *shard_bounds, int32_t n_shards,
+                                                void *k_tail, void *v_tail, int64_t tail_len, int64_t tail_cap,
+                                                int32_t hq, int32_t hkv, int32_t d,
+                                                star_dtype_t dt, float scale,
+                                                void *o, float *lse, hipStream_t stream);
 
 /*
  * E4M3 context KV cache.

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -112,6 +112,28 @@ def test_decode_validation(lib):
     assert d(*args(good, 0, 0, 8, 1 << 30)) == 1                   # no shards
     assert d(*args(good, 65, 0, 8, 1 << 30)) == 1                  # too many shards
     assert d(*args(good, 2, 0, 8, 16)) == 4                        # workspace too small
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-workspace decode step checks its arguments like star_decode_step and refuses, before
+    any device call, a shape whose chunk partials do not fit its static scratch."""
+    d = lib.star_decode_step_noalloc
+    B = ctypes.c_int64 * 3
+    good = B(0, 50, 100)
+
+    def args(bounds=good, n_sh=2, tl=0, tc=8, hq=4, hkv=2, dim=128, L=100):
+        return (FAKE, FAKE, FAKE, FAKE, FAKE, L, bounds, n_sh, FAKE, FAKE, tl, tc, hq, hkv, dim, 1, 0.1, FAKE, NULL,
+                NULL)
+    assert d(*args(bounds=B(0, 60, 50))) == 1                      # not monotone
+    assert d(*args(tl=8)) == 1                                     # tail full
+    assert d(*args(n_sh=65)) == 1                                  # too many shards
+    assert d(*args(hq=5)) == 1                                     # hq % hkv
+    many = (ctypes.c_int64 * 65)(*[i * 64 for i in range(65)])
+    assert d(*args(bounds=many, n_sh=64, L=4096, hq=1024, hkv=64)) == 4   # partials beyond the scratch
+    assert b"static scratch" in lib.star_last_error()
+    assert d(*args(hq=2048, hkv=2048)) == 4                        # more kv heads than counters
+    need = lib.star_decode_workspace_bytes(4096, 8, 64, 1024, 64, 128)
+    assert need > 8 << 20
 
 
 def test_kv_fp8_validation(lib):
