@@ -8,7 +8,7 @@ resident in HBM:
            then decode_steps x star_decode_step (append + split-KV partials + merge).
 
 Prints ONE JSON line.  `value` is context tokens per second of the whole step
-(L / step time).  `roofline` describes the dominant kernel (the Phase-1 MFMA kernel):
+(L / step time, `value_is` says so); `phase1.context_tokens_per_s` is the Phase-1 rate alone.  `roofline` describes the dominant kernel (the Phase-1 MFMA kernel):
 algorithmic flops per launch / its average launch time measured with HIP events on the
 launch stream, against the bf16 dense MFMA peak.  `decode` reports the decode step's
 K/V stream rate (warm: inside the step; cold: after overwriting 1 GiB and reading it back,
@@ -16,7 +16,11 @@ so the 256 MB last-level cache holds no K/V and no dirty lines).  `decode_kv8` r
 same decode steps over an E4M3 context cache (quantised once, after the step; its time is
 reported too) against the same bytes model with 1-byte context elements, and the query
 phase over that cache (star_phase2_query_kv8).  `cpu_baseline`
-times the fp64 oracle on a bounded sample of Phase-1 rows on the host's cores.
+times the fp64 oracle on a bounded sample of the same step on the host's cores: seeded
+Phase-1 rows, sampled query rows and whole decode steps.
+
+The default workload is the largest one, 8b_1m (L = 1,048,576, block = anchor = 65,536,
+16 shards); `--config` selects another.
 """
 from __future__ import annotations
 
@@ -36,7 +40,7 @@ METRIC = "Phase-1 context tokens/s + MFMA %peak; Phase-2 decode KV GB/s (%HBM), 
 PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
 PHASE1_KERNEL = "attn_mfma_kernel<0, 128, false>"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "phase1_8b_32k_traffic.txt")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_phase1_amd", "csrc", f)
                   for f in ("prefill.hip", "common.h", "internal.h")]
 
@@ -58,12 +62,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(launch_flops_unit_bytes=None):
-    """HBM bytes per Phase-1 launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def traffic_profile_path(workload: str) -> str:
+    """The committed rocprofv3 counter summary of the Phase-1 kernel on one workload."""
+    return os.path.join(PROFILE_DIR, "phase1_%s_traffic.txt" % workload)
+
+
+def read_traffic(workload: str):
+    """HBM bytes per Phase-1 launch on `workload` from the committed rocprofv3 counter
+    summary, if one was taken on that workload and on the current kernel source; else None."""
+    path = traffic_profile_path(workload)
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_TRAFFIC).read()
+    text = open(path).read()
     m = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not b or m.group(1) != kernel_source_hash():
@@ -76,11 +86,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="8b_32k")
+    ap.add_argument("--config", default="8b_1m")
     ap.add_argument("--block", type=int, default=None, help="override the workload's block size")
     ap.add_argument("--anchor", type=int, default=None, help="override the workload's anchor size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0,
+                    help="host CPU time budget of the oracle baseline (split between the two phases)")
     ap.add_argument("--cold-reps", type=int, default=8)
     ap.add_argument("--no-kv8", action="store_true", help="skip the E4M3 context-cache decode leg")
     ap.add_argument("--only", choices=["all", "phase1", "decode"], default="all",
@@ -206,6 +217,7 @@ def main():
     # flush buffer, so the timed step neither finds K/V cached nor pays for writing back
     # the flush's dirty lines.  Nothing synchronises between these launches and the timed
     # step, so the GPU is busy until the step starts and host launch time is not counted.
+    print("bench: cold-cache decode steps", file=sys.stderr, flush=True)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     cold = []
@@ -223,6 +235,7 @@ def main():
     # ---- E4M3 context cache: quantise the context once, then the decode steps over it
     kv8 = None
     if cfg.dtype == "bf16" and not args.no_kv8:
+        print("bench: E4M3 context cache leg", file=sys.stderr, flush=True)
         ks = torch.empty((cfg.hkv,), dtype=torch.float32, device=dev)
         vs = torch.empty_like(ks)
         k8 = torch.empty((cfg.hkv, cfg.L, cfg.d), dtype=torch.uint8, device=dev)
@@ -304,12 +317,14 @@ def main():
     dec_avg = float(np.mean(dec_ms))
     warm_bw = dec_bytes / (dec_avg * 1e-3)
     cold_bw = sum(bb for _, bb in cold) / (sum(ms for ms, _ in cold) * 1e-3)
-    traffic = read_traffic()
+    traffic = read_traffic(cfg.name)
 
     result = {
         "metric": METRIC,
         "value": cfg.L / (ms_per_step * 1e-3),
         "unit": "context tokens/s",
+        "value_is": "context tokens per second of the whole step: L / (Phase 1 + query phase + every "
+                    "decode step); the Phase-1 rate alone is phase1.context_tokens_per_s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -339,35 +354,97 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
+        print("bench: CPU oracle baseline (about %.0f s)" % args.cpu_seconds, file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, x, bounds, k_tail, v_tail, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cfg, q, k, v, seconds):
-    """fp64 oracle on the host: Phase-1 rows (all q heads each) for about `seconds` of CPU
-    time, scaled to context tokens/s."""
+def host_threads() -> tuple[int, int]:
+    """(CPUs this process may run on, oracle threads).  The oracle takes at most 16 threads,
+    one GPU's share of a host, whatever the machine reports."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return avail, max(1, min(16, avail))
+
+
+def cpu_baseline(cfg, x, bounds, k_tail, v_tail, seconds):
+    """The fp64 oracle on the host over a bounded sample of one bench step, scaled to the
+    whole step: about half of `seconds` on seeded-random Phase-1 rows (all q heads each), then
+    sampled query rows (every partition, all q heads) and whole decode steps (all q heads over
+    every context token and the query host's cache).  Each leg takes at least one unit."""
     import numpy as np
     import torch
 
     import oracle
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    avail, threads = host_threads()
+    q, k, v = x["q_ctx"], x["k_ctx"], x["v_ctx"]
     kh, vh = k.cpu(), v.cpu()
+    kt, vt = k_tail.cpu(), v_tail.cpu()
     rng = np.random.default_rng(cfg.seed)
-    done, elapsed, batch = 0, 0.0, 32
-    while elapsed < seconds:
-        rows = np.sort(rng.choice(cfg.L, size=batch, replace=False)).astype(np.int64)
+
+    # Phase 1: seeded-random context rows, batches doubling until the budget is spent
+    p1_rows, p1_s, batch = 0, 0.0, 8
+    while p1_s < 0.5 * seconds:
+        rows = np.sort(rng.choice(cfg.L, size=min(batch, cfg.L), replace=False)).astype(np.int64)
         qs = q[:, torch.from_numpy(rows).to(q.device)].cpu()
         t0 = time.perf_counter()
         oracle.phase1(qs, kh, vh, cfg.block, cfg.anchor, rows=rows, q_sampled=True, threads=threads)
-        elapsed += time.perf_counter() - t0
-        done += batch
+        p1_s += time.perf_counter() - t0
+        p1_rows += rows.size
         batch = min(batch * 2, 1024)
-    return {"value": done / elapsed, "unit": "context tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d seeded-random Phase-1 context rows x all %d q heads of %s, fp64 C oracle, %.1f s on %s; "
-                      "value = rows per second, i.e. the full context's rate extrapolated from the sample "
-                      "(uniformly drawn rows carry the context's mean cost per row)"
-                      % (done, cfg.hq, cfg.name, elapsed, cpu_model())}
+
+    # Phase 2 query phase: one query row at a time (its partial over every context shard, its
+    # causal partial over the query tokens before it, the merge), rows in seeded order
+    kq, vq = kt[:, :cfg.lq], vt[:, :cfg.lq]
+    qq = x["q_qry"].cpu()
+    q_rows, q_s = 0, 0.0
+    for i in rng.permutation(cfg.lq):
+        qi = qq[:, int(i):int(i) + 1]
+        t0 = time.perf_counter()
+        parts = [oracle.partial(qi, kh, vh, lo, hi, -1, threads=threads) for lo, hi in zip(bounds[:-1], bounds[1:])]
+        parts.append(oracle.partial(qi, kq, vq, 0, cfg.lq, int(i), threads=threads))
+        oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]),
+                     np.stack([p[2] for p in parts]))
+        q_s += time.perf_counter() - t0
+        q_rows += 1
+        if q_s >= 0.15 * seconds:
+            break
+
+    # Phase 2 decode: whole steps t = 0, 1, ... (the query host's cache as the step saw it)
+    dec_steps, dec_s = 0, 0.0
+    for t in range(cfg.decode_steps):
+        qt = x["q_dec"][t].cpu()
+        t0 = time.perf_counter()
+        oracle.phase2_decode(qt, kh, vh, bounds, kt, vt, cfg.lq + t + 1, threads=threads)
+        dec_s += time.perf_counter() - t0
+        dec_steps += 1
+        if dec_s >= 0.35 * seconds:
+            break
+
+    p1_row_s = p1_s / p1_rows
+    q_row_s = q_s / q_rows
+    dec_step_s = dec_s / dec_steps
+    step_s = p1_row_s * cfg.L + q_row_s * cfg.lq + dec_step_s * cfg.decode_steps
+    return {"value": cfg.L / step_s, "unit": "context tokens/s", "cores": threads, "kind": "oracle",
+            "threads": threads, "host_cpus": avail, "host_cpus_reported": os.cpu_count(),
+            "cpu_model": cpu_model(),
+            "sample": "%s, fp64 C oracle on %d threads (%s; %d CPUs available, os.cpu_count() %s): %d "
+                      "seeded-random Phase-1 context rows x all %d q heads (%.1f s), %d of %d query rows "
+                      "(%.1f s), %d of %d decode steps (%.1f s); value = L / (per-row Phase-1 time x L + "
+                      "per-row query time x lq + per-step decode time x T), i.e. the whole step extrapolated "
+                      "from the sample (uniformly drawn rows carry the context's mean cost per row)"
+                      % (cfg.name, threads, cpu_model(), avail, os.cpu_count(), p1_rows, cfg.hq, p1_s, q_rows,
+                         cfg.lq, q_s, dec_steps, cfg.decode_steps, dec_s),
+            "phase1": {"rows": p1_rows, "seconds": p1_s, "context_tokens_per_s": 1.0 / p1_row_s,
+                       "extrapolated_s": p1_row_s * cfg.L},
+            "query_phase": {"rows": q_rows, "seconds": q_s, "extrapolated_s": q_row_s * cfg.lq},
+            "decode": {"steps": dec_steps, "seconds": dec_s, "s_per_token": dec_step_s,
+                       "kv_GBps": cfg.decode_step_bytes(0) / dec_step_s / 1e9,
+                       "extrapolated_s": dec_step_s * cfg.decode_steps},
+            "step_s_extrapolated": step_s}
 
 
 def cpu_model() -> str:
