@@ -195,6 +195,31 @@ def _kv_view(t, q, name, hkv, d):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _partition_stride(k, v, n_kv: int, kv_head_stride, d: int) -> int:
+    """The element stride between kv heads of a partition view pair, checked against both
+    views: k and v must share it, hold n_kv tokens per head and, from their first element,
+    reach (hkv - 1) * stride + n_kv * d elements inside their storage."""
+    hkv = k.shape[0]
+    stride = k.stride(0) if kv_head_stride is None else int(kv_head_stride)
+    if v.shape[0] != hkv:
+        raise ValueError("k and v views must have the same number of kv heads")
+    for t, name in ((k, "k"), (v, "v")):
+        if t.dim() != 3 or t.shape[-1] != d or (t.shape[1] > 1 and t.stride(1) != d):
+            raise ValueError("%s must be a [Hkv, n, %d] view whose tokens are %d elements apart" % (name, d, d))
+    if hkv > 1 and (k.stride(0) != stride or v.stride(0) != stride):
+        raise ValueError("kv_head_stride %d must equal k.stride(0) (%d) and v.stride(0) (%d)"
+                         % (stride, k.stride(0), v.stride(0)))
+    if n_kv > 0:
+        for t, name in ((k, "k"), (v, "v")):
+            if t.shape[1] < n_kv:
+                raise ValueError("%s view holds %d tokens, n_kv is %d" % (name, t.shape[1], n_kv))
+            avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+            if (hkv - 1) * stride + n_kv * d > avail:
+                raise ValueError("%s view: %d kv heads of %d tokens at stride %d run past its storage"
+                                 % (name, hkv, n_kv, stride))
+    return stride
+
+
 def _kv8_view(t, name, hkv, d):
     """Base pointer of a (possibly strided) uint8 E4M3 partition view [Hkv, n, d]."""
     torch = _torch()
@@ -205,13 +230,14 @@ def _kv8_view(t, name, hkv, d):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def star_phase2_partial(q, k, v, kv_head_stride: int, n_kv: int, causal_offset: int = -1,
+def star_phase2_partial(q, k, v, kv_head_stride, n_kv: int, causal_offset: int = -1,
                         a_out=None, m_out=None, l_out=None, workspace=None, scale=None, stream=None):
     """Local attention of q [Hq,rows,d] over one KV partition.
 
     k/v are device views [Hkv, >=n_kv, d] whose first element is partition token 0 of kv
-    head 0 (e.g. ``k_ctx[:, lo:]``), with ``kv_head_stride`` elements between kv heads.
-    Returns fp32 (A [Hq,rows,d], m [Hq,rows], l [Hq,rows]).
+    head 0 (e.g. ``k_ctx[:, lo:]``), with ``kv_head_stride`` elements between kv heads (None:
+    k.stride(0); it must equal both views' stride).  Returns fp32 (A [Hq,rows,d], m [Hq,rows],
+    l [Hq,rows]).
     """
     torch = _torch()
     hq, rows, d = q.shape
@@ -223,8 +249,7 @@ def star_phase2_partial(q, k, v, kv_head_stride: int, n_kv: int, causal_offset: 
         m_out = torch.empty((hq, rows), dtype=torch.float32, device=dev)
     if l_out is None:
         l_out = torch.empty((hq, rows), dtype=torch.float32, device=dev)
-    if n_kv > 0 and k.shape[1] < n_kv:
-        raise ValueError("k view holds %d tokens, n_kv is %d" % (k.shape[1], n_kv))
+    kv_head_stride = _partition_stride(k, v, n_kv, kv_head_stride, d)
     need = star_phase2_workspace_bytes(rows, n_kv, hq, hkv, d)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -238,10 +263,11 @@ def star_phase2_partial(q, k, v, kv_head_stride: int, n_kv: int, causal_offset: 
     return a_out, m_out, l_out
 
 
-def star_phase2_partial_kv8(q, k8, v8, k_scale, v_scale, kv_head_stride: int, n_kv: int, causal_offset: int = -1,
+def star_phase2_partial_kv8(q, k8, v8, k_scale, v_scale, kv_head_stride, n_kv: int, causal_offset: int = -1,
                             a_out=None, m_out=None, l_out=None, workspace=None, scale=None, stream=None):
     """star_phase2_partial over a partition of E4M3 codes: k8/v8 are uint8 device views
-    [Hkv, >=n_kv, d] (e.g. ``k8_ctx[:, lo:]``) with fp32 scales [Hkv]; q is bf16."""
+    [Hkv, >=n_kv, d] (e.g. ``k8_ctx[:, lo:]``) with fp32 scales [Hkv]; q is bf16.
+    kv_head_stride as in star_phase2_partial (None: k8.stride(0))."""
     torch = _torch()
     hq, rows, d = q.shape
     hkv = k8.shape[0]
@@ -252,8 +278,7 @@ def star_phase2_partial_kv8(q, k8, v8, k_scale, v_scale, kv_head_stride: int, n_
         m_out = torch.empty((hq, rows), dtype=torch.float32, device=dev)
     if l_out is None:
         l_out = torch.empty((hq, rows), dtype=torch.float32, device=dev)
-    if n_kv > 0 and k8.shape[1] < n_kv:
-        raise ValueError("k8 view holds %d tokens, n_kv is %d" % (k8.shape[1], n_kv))
+    kv_head_stride = _partition_stride(k8, v8, n_kv, kv_head_stride, d)
     need = star_phase2_workspace_bytes(rows, n_kv, hq, hkv, d)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -79,7 +79,7 @@ star_status_t check_decode(const void* q_new, const void* k_new, const void* v_n
     if (tail_len < 0 || tail_cap < 1 || tail_len + 1 > tail_cap)
         return fail(STAR_ERR_INVALID_ARG, "need 0 <= tail_len < tail_cap (tail_len %lld, tail_cap %lld)",
                     (long long)tail_len, (long long)tail_cap);
-    if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+    if (!(std::isfinite(scale) && scale >= 0.f)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite and >= 0");
     star_status_t s = check_heads(hq, hkv, d, dt);
     if (s != STAR_OK) return s;
     if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_tail) || !aligned16(v_tail) ||
@@ -103,7 +103,7 @@ star_status_t check_query(const void* q, int32_t rows, int64_t L, const int64_t*
     if (tail_len < rows || tail_len > tail_cap)
         return fail(STAR_ERR_INVALID_ARG, "need rows <= tail_len <= tail_cap (rows %d, tail_len %lld, tail_cap %lld)",
                     rows, (long long)tail_len, (long long)tail_cap);
-    if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+    if (!(std::isfinite(scale) && scale >= 0.f)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite and >= 0");
     star_status_t s = check_heads(hq, hkv, d, dt);
     if (s != STAR_OK) return s;
     if (!aligned16(q) || !aligned16(k_tail) || !aligned16(v_tail) || !aligned16(o) ||
@@ -314,7 +314,7 @@ star_status_t star_phase1_encode(const void* q, const void* k, const void* v, vo
         if (anchor < 0 || anchor > block)
             return fail(STAR_ERR_INVALID_ARG, "anchor (%lld) must satisfy 0 <= anchor <= block (%lld)",
                         (long long)anchor, (long long)block);
-        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        if (!(std::isfinite(scale) && scale >= 0.f)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite and >= 0");
         star_status_t s = check_heads(hq, hkv, d, dt);
         if (s != STAR_OK) return s;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -365,7 +365,7 @@ star_status_t star_phase2_partial(const void* q, int32_t rows, const void* k, co
         if (n_kv > 0 && (!k || !v)) return fail(STAR_ERR_INVALID_ARG, "k and v must be non-null when n_kv > 0");
         if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
         if (n_kv < 0) return fail(STAR_ERR_INVALID_ARG, "n_kv must be >= 0");
-        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        if (!(std::isfinite(scale) && scale >= 0.f)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite and >= 0");
         star_status_t s = check_heads(hq, hkv, d, dt);
         if (s != STAR_OK) return s;
         if (hkv > 1 && kv_head_stride < n_kv * d)
@@ -404,7 +404,7 @@ star_status_t star_phase2_partial_kv8(const void* q, int32_t rows, const void* k
         if (n_kv > 0 && (!k8 || !v8)) return fail(STAR_ERR_INVALID_ARG, "k8 and v8 must be non-null when n_kv > 0");
         if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
         if (n_kv < 0) return fail(STAR_ERR_INVALID_ARG, "n_kv must be >= 0");
-        if (!std::isfinite(scale)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite");
+        if (!(std::isfinite(scale) && scale >= 0.f)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite and >= 0");
         star_status_t s = check_heads(hq, hkv, d, dt);
         if (s != STAR_OK) return s;
         if (kv_head_stride < 0) return fail(STAR_ERR_INVALID_ARG, "kv_head_stride must be >= 0");

@@ -16,7 +16,9 @@
  *   head h / (Hq / Hkv) (contiguous groups).  Hq must be a multiple of Hkv.
  * Scale.  Scores are scale * <q, k>; pass scale = 1/sqrt(d) for the pages'
  *   attention ([SUM] 3.4 "The Attention Decomposition").  All logs and
- *   log-sum-exps are natural logs of the scaled scores.
+ *   log-sum-exps are natural logs of the scaled scores.  scale must be finite
+ *   and >= 0 (else STAR_ERR_INVALID_ARG): the kernels take a row's largest
+ *   score as scale times its largest dot product.
  * Softmax statistics.  A partial result over a key partition is (A, m, l):
  *   A is normalised over that partition alone, m is the largest scaled score
  *   and l = sum exp(score - m), so the pages' s_h equals e^m * l.  An empty

@@ -260,3 +260,46 @@ def test_host_tensors_are_rejected(lib):
         sa.star_phase2_query(q, k, k.clone(), [0, 8], k.clone(), k.clone(), 8)
     with pytest.raises(ValueError, match="device tensor"):
         sa.star_phase2_partial(q, k, k.clone(), 8 * 128, 8)
+
+
+def test_partition_views_are_checked_before_any_call(lib):
+    """The partial bindings take the kv head stride from the views (or check the one given
+    against both) and refuse views that are short or run past their storage."""
+    import torch
+    q = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 64, 128, dtype=torch.bfloat16)
+    v = torch.zeros(2, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must equal"):
+        sa.star_phase2_partial(q, k, v, 65 * 128, 64)                       # stride not the views'
+    with pytest.raises(ValueError, match="must equal"):
+        sa.star_phase2_partial(q, k, torch.zeros(2, 80, 128, dtype=torch.bfloat16)[:, :64], None, 64)  # v's stride
+    with pytest.raises(ValueError, match="elements apart"):
+        sa.star_phase2_partial(q, k, v[:, ::2], None, 32)                  # v tokens not d apart
+    with pytest.raises(ValueError, match="v view holds"):
+        sa.star_phase2_partial(q, k, v[:, :16], None, 32)                  # v shorter than n_kv
+    with pytest.raises(ValueError, match="k view holds"):
+        sa.star_phase2_partial(q, k[:, 40:], v[:, 40:], None, 32)          # 24 tokens left, 32 asked
+    k8 = torch.zeros(2, 64, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="must equal"):
+        sa.star_phase2_partial_kv8(q, k8, k8.clone(), torch.ones(2), torch.ones(2), 100, 64)
+    with pytest.raises(ValueError, match="device tensor"):                 # valid views reach the device check
+        sa.star_phase2_partial(q, k, v, None, 64)
+
+
+def test_negative_scale_is_rejected(lib):
+    """A negative scale would flip which score is a row's largest; every entry point refuses it."""
+    st = lib.star_phase1_encode(FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 1, ctypes.c_float(-0.1), NULL)
+    assert st == 1 and b"scale" in lib.star_last_error()
+    p = lib.star_phase2_partial
+    assert p(FAKE, 4, FAKE, FAKE, 1024, 8, -1, 4, 2, 128, 1, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, NULL, 0,
+             NULL) == 1
+    B = ctypes.c_int64 * 3
+    good = B(0, 50, 100)
+    d = lib.star_decode_step
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 100, good, 2, FAKE, FAKE, 0, 8, 4, 2, 128, 1, ctypes.c_float(-0.5),
+             FAKE, NULL, FAKE, 1 << 30, NULL) == 1
+    q = lib.star_phase2_query
+    assert q(FAKE, 8, FAKE, FAKE, 100, good, 2, FAKE, FAKE, 8, 8, 4, 2, 128, 1, ctypes.c_float(-0.5), FAKE, NULL,
+             FAKE, 1 << 30, NULL) == 1
+    assert lib.star_phase1_encode(FAKE, FAKE, FAKE, FAKE, NULL, 64, 32, 32, 4, 2, 128, 1, ctypes.c_float(0.0),
+                                  NULL) != 1 or b"scale" not in lib.star_last_error()
