@@ -463,39 +463,6 @@ decode_kernel(const DecodeArgs p) {
     if (tid == 0) __hip_atomic_store(&p.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-bool decode_bf16_supported(int d, int hq, int hkv) {
-    if ((d != 64 && d != 128) || hkv < 1 || hq % hkv) return false;
-    const int G = hq / hkv;
-    return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
-}
-
-int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv) {
-    // About one context chunk per compute unit (256 CUs), all in one round: each kv head gets
-    // up to 272/hkv - 1 context chunks, spread over its shards by length, plus
-    // its query-host chunk(s).  Chunks are a multiple of the 4 x 32 keys one pass covers.
-    const int64_t L = shard_bounds[n_shards] - shard_bounds[0];
-    int64_t budget = 272 / hkv - 1;
-    if (budget < n_shards) budget = n_shards;
-    int64_t ch = 128;
-    for (int r = 0; r < n_shards; ++r) {
-        const int64_t len = shard_bounds[r + 1] - shard_bounds[r];
-        if (len <= 0) continue;
-        int64_t cr = budget * len / (L > 0 ? L : 1);
-        if (cr < 1) cr = 1;
-        const int64_t need = (len + cr - 1) / cr;
-        if (need > ch) ch = need;
-    }
-    return (ch + 127) / 128 * 128;
-}
-
-int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv) {
-    // The plan above gives each shard at most budget*len/L chunks (at least 1), hence at
-    // most budget + n_shards context chunks, and the query host at most ceil(tail_cap/128).
-    int64_t budget = 272 / hkv - 1;
-    if (budget < n_shards) budget = n_shards;
-    return budget + n_shards + (tail_cap + 127) / 128;
-}
-
 namespace {
 template <int D, bool KV8>
 hipError_t launch_decode_g(const DecodeArgs& a, dim3 gd, hipStream_t stream) {

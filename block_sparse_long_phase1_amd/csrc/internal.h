@@ -4,26 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace star {
+#include "host_plan.h"
 
-// Key partitions of one Phase-2 partial launch.  Partition i holds keys [0, n_kv[i]) at
-// k[i] / v[i], kv heads head_stride[i] elements apart; query row r sees token t iff
-// causal[i] < 0 or t <= causal[i] + r.  Partitions are cut into splits of split_len keys;
-// partition i owns global splits [split_prefix[i], split_prefix[i + 1]).
-constexpr int kMaxParts = 65;
-struct PartPlan {
-    int n_parts;
-    int64_t split_len;
-    const void* k[kMaxParts];   // bf16 elements, or E4M3 codes for parts [0, n_f8)
-    const void* v[kMaxParts];
-    int64_t head_stride[kMaxParts];
-    int64_t n_kv[kMaxParts];
-    int64_t causal[kMaxParts];
-    int32_t split_prefix[kMaxParts + 1];
-    int n_f8;                   // parts [0, n_f8) hold E4M3 codes (with per-kv-head scales)
-    const float* k_scale;       // [hkv], for E4M3 parts
-    const float* v_scale;
-};
+namespace star {
 
 // Arguments of the bf16 MFMA attention kernel (Phase 1 and Phase-2 partials).
 struct AttnMfmaArgs {
@@ -49,21 +32,9 @@ struct AttnMfmaArgs {
     PartPlan plan;
 };
 
-// bf16 MFMA kernels: head dim 64 or 128, G = hq / hkv dividing 256.
-bool attn_mfma_supported(int d, int hq, int hkv);
-// Largest per-kv-head token count the MFMA kernel addresses with 32-bit offsets.
-int64_t attn_mfma_max_tokens(int d);
-
 hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               uint16_t* o, float* lse, int64_t L, int64_t block, int64_t anchor,
                               int hq, int hkv, int d, float scale, hipStream_t stream);
-
-// Cut the partitions of `plan` (n_parts, n_kv set) into key splits: fills split_len and
-// split_prefix and returns the number of query-row tiles.  Splits aim at one workgroup
-// per compute unit with at least 8 key tiles each.
-int partial_mfma_plan(PartPlan& plan, int32_t rows, int32_t hq, int32_t hkv);
-// Upper bound on the splits partial_mfma_plan makes for n_parts partitions.
-int64_t partial_mfma_max_splits(int32_t rows, int32_t hq, int32_t hkv, int n_parts);
 
 // Partials of every split of `plan` into a_out / m_out / l_out (global split order).
 hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, int d, float scale,
@@ -79,19 +50,6 @@ hipError_t launch_merge(const float* a, const float* m, const float* l, int n_pa
 // Split-KV decode (bf16, d = 64 or 128): chunk partials for every kv head, the append of the
 // new token into the query host's cache, and the log-space merge by the last chunk of
 // each kv head (tickets: hkv zero-initialised counters, left at zero).
-struct DecodeChunkPlan {
-    int n_shards;
-    int64_t chunk;                 // keys per chunk
-    int64_t shard_lo[65];          // shard token bounds
-    int32_t chunk_prefix[66];      // first chunk index of each shard; [n_shards] = first tail chunk
-    int32_t n_chunks;              // total chunks including the tail ones
-};
-
-bool decode_bf16_supported(int d, int hq, int hkv);
-// Keys per decode chunk for a shard layout, and an upper bound on the chunk count of any
-// call with at most tail_cap query-host tokens and n_shards shards.
-int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv);
-int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv);
 // k8 / v8 non-null: the context partitions are E4M3 codes with per-kv-head scales
 // k_scale / v_scale (k_ctx / v_ctx unused); null: bf16 k_ctx / v_ctx.
 hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,

@@ -41,8 +41,8 @@ namespace star {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kBN = 64;          // keys per tile
-constexpr int kQPB = 256;        // queries per workgroup
+constexpr int kBN = kAttnKeysPerTile;        // keys per tile (64)
+constexpr int kQPB = kAttnQueriesPerGroup;   // queries per workgroup (256)
 constexpr int kKB = kBN / 32;    // 32-key MFMA blocks per tile
 // LDS tile layout for head dim D (rows of 2D bytes).  A tile's 64 key rows sit in 1 KB
 // blocks of 1024/(2D) rows: with NB = 64 / (rows per block) blocks, block b holds rows
@@ -611,14 +611,6 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
 
 // ------------------------------------------------------------------------- launchers
 
-bool attn_mfma_supported(int d, int hq, int hkv) {
-    if ((d != 64 && d != 128) || hkv < 1 || hq % hkv) return false;
-    const int G = hq / hkv;
-    return G >= 1 && G <= kQPB && (kQPB % G) == 0;
-}
-
-int64_t attn_mfma_max_tokens(int d) { return ((int64_t)1 << 31) / d; }
-
 hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               uint16_t* o, float* lse, int64_t L, int64_t block, int64_t anchor,
                               int hq, int hkv, int d, float scale, hipStream_t stream) {
@@ -648,39 +640,6 @@ hipError_t launch_phase1_mfma(const uint16_t* q, const uint16_t* k, const uint16
     else if (d == 64) hipLaunchKernelGGL((attn_mfma_kernel<0, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
-}
-
-static int partial_splits_wanted(int32_t rows, int32_t hq, int32_t hkv, int* n_row_tiles) {
-    const int G = hq / hkv;
-    const int rw = kQPB / G;
-    const int nrt = (rows + rw - 1) / rw;
-    const int64_t base = (int64_t)hkv * nrt;
-    *n_row_tiles = nrt;
-    // One workgroup of eight waves fills a compute unit; aim for one per CU (256).
-    return (int)(base >= 256 ? 1 : 256 / base);
-}
-
-int partial_mfma_plan(PartPlan& plan, int32_t rows, int32_t hq, int32_t hkv) {
-    int nrt;
-    const int want = partial_splits_wanted(rows, hq, hkv, &nrt);
-    int64_t total_tiles = 0;
-    for (int i = 0; i < plan.n_parts; ++i) total_tiles += (plan.n_kv[i] + kBN - 1) / kBN;
-    int64_t tps = (total_tiles + want - 1) / want;
-    if (tps < 8) tps = 8;   // enough tiles per split to amortise the partial's write and merge
-    plan.split_len = tps * kBN;
-    plan.split_prefix[0] = 0;
-    for (int i = 0; i < plan.n_parts; ++i) {
-        int64_t ns = (plan.n_kv[i] + plan.split_len - 1) / plan.split_len;
-        if (ns < 1) ns = 1;   // an empty partition still reports its (empty) partial
-        plan.split_prefix[i + 1] = plan.split_prefix[i] + (int32_t)ns;
-    }
-    return nrt;
-}
-
-int64_t partial_mfma_max_splits(int32_t rows, int32_t hq, int32_t hkv, int n_parts) {
-    int nrt;
-    // ceil(tiles_i / tps) <= tiles_i / tps + 1 and sum(tiles_i) / tps <= want.
-    return (int64_t)partial_splits_wanted(rows, hq, hkv, &nrt) + n_parts;
 }
 
 hipError_t launch_partial_mfma(const uint16_t* q, int32_t rows, int hq, int hkv, int d, float scale,

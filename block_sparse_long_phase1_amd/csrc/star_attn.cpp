@@ -3,113 +3,16 @@
 // enqueues anything, never allocates device memory and never synchronises.
 #include "star_attn.h"
 
-#include <cmath>
-#include <cstdarg>
-#include <cstdio>
 #include <mutex>
-#include <string>
 
 #include "internal.h"
 
+using namespace star::host;
+
 namespace {
-
-thread_local std::string g_last_error;
-
-star_status_t fail(star_status_t s, const char* fmt, ...) {
-    char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
-    g_last_error = buf;
-    return s;
-}
-
-star_status_t ok() {
-    g_last_error.clear();
-    return STAR_OK;
-}
 
 star_status_t hip_fail(hipError_t e, const char* where) {
     return fail(STAR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int elem_bytes(star_dtype_t dt) { return dt == STAR_BF16 ? 2 : 4; }
-
-star_status_t check_heads(int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt) {
-    if (hq < 1 || hkv < 1) return fail(STAR_ERR_INVALID_ARG, "hq (%d) and hkv (%d) must be >= 1", hq, hkv);
-    if (hq % hkv) return fail(STAR_ERR_INVALID_ARG, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
-    if (d < 1) return fail(STAR_ERR_INVALID_ARG, "d (%d) must be >= 1", d);
-    if (dt != STAR_F32 && dt != STAR_BF16) return fail(STAR_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
-    if (d > 256 || d % 4)
-        return fail(STAR_ERR_UNSUPPORTED, "head dim %d not supported (need d %% 4 == 0 and d <= 256)", d);
-    return STAR_OK;
-}
-
-constexpr size_t kAlign = 256;
-size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-// Workspace layout of split partials: A [n][rows][d] fp32, then m [n][rows], then l [n][rows].
-size_t partials_bytes(int64_t n_parts, int64_t n_rows, int32_t d) {
-    return round_up((size_t)n_parts * n_rows * d * 4) + 2 * round_up((size_t)n_parts * n_rows * 4);
-}
-void partials_ptrs(void* ws, int64_t n_parts, int64_t n_rows, int32_t d, float** a, float** m, float** l) {
-    char* base = static_cast<char*>(ws);
-    *a = reinterpret_cast<float*>(base);
-    *m = reinterpret_cast<float*>(base + round_up((size_t)n_parts * n_rows * d * 4));
-    *l = reinterpret_cast<float*>(base + round_up((size_t)n_parts * n_rows * d * 4) +
-                                  round_up((size_t)n_parts * n_rows * 4));
-}
-
-// Checks shared by both decode entry points (the context pointers are checked by each).
-star_status_t check_decode(const void* q_new, const void* k_new, const void* v_new, int64_t L,
-                           const int64_t* shard_bounds, int32_t n_shards, const void* k_tail, const void* v_tail,
-                           int64_t tail_len, int64_t tail_cap, int32_t hq, int32_t hkv, int32_t d, star_dtype_t dt,
-                           float scale, const void* o, const float* lse) {
-    if (!q_new || !k_new || !v_new || !k_tail || !v_tail || !o || !shard_bounds)
-        return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
-    if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
-    if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
-    if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
-        return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
-    for (int r = 0; r < n_shards; ++r)
-        if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
-    if (tail_len < 0 || tail_cap < 1 || tail_len + 1 > tail_cap)
-        return fail(STAR_ERR_INVALID_ARG, "need 0 <= tail_len < tail_cap (tail_len %lld, tail_cap %lld)",
-                    (long long)tail_len, (long long)tail_cap);
-    if (!(std::isfinite(scale) && scale >= 0.f)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite and >= 0");
-    star_status_t s = check_heads(hq, hkv, d, dt);
-    if (s != STAR_OK) return s;
-    if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_tail) || !aligned16(v_tail) ||
-        !aligned16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-        return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-    return STAR_OK;
-}
-
-// Checks shared by both query-phase entry points (the context pointers are checked by each).
-star_status_t check_query(const void* q, int32_t rows, int64_t L, const int64_t* shard_bounds, int32_t n_shards,
-                          const void* k_tail, const void* v_tail, int64_t tail_len, int64_t tail_cap, int32_t hq,
-                          int32_t hkv, int32_t d, star_dtype_t dt, float scale, const void* o, const float* lse) {
-    if (!q || !k_tail || !v_tail || !o || !shard_bounds) return fail(STAR_ERR_INVALID_ARG, "required pointer is null");
-    if (L < 1) return fail(STAR_ERR_INVALID_ARG, "L must be >= 1");
-    if (rows < 1) return fail(STAR_ERR_INVALID_ARG, "rows (%d) must be >= 1", rows);
-    if (n_shards < 1 || n_shards > 64) return fail(STAR_ERR_INVALID_ARG, "n_shards (%d) must be in [1, 64]", n_shards);
-    if (shard_bounds[0] != 0 || shard_bounds[n_shards] != L)
-        return fail(STAR_ERR_INVALID_ARG, "shard bounds must start at 0 and end at L");
-    for (int r = 0; r < n_shards; ++r)
-        if (shard_bounds[r + 1] < shard_bounds[r]) return fail(STAR_ERR_INVALID_ARG, "shard bounds must be non-decreasing");
-    if (tail_len < rows || tail_len > tail_cap)
-        return fail(STAR_ERR_INVALID_ARG, "need rows <= tail_len <= tail_cap (rows %d, tail_len %lld, tail_cap %lld)",
-                    rows, (long long)tail_len, (long long)tail_cap);
-    if (!(std::isfinite(scale) && scale >= 0.f)) return fail(STAR_ERR_INVALID_ARG, "scale must be finite and >= 0");
-    star_status_t s = check_heads(hq, hkv, d, dt);
-    if (s != STAR_OK) return s;
-    if (!aligned16(q) || !aligned16(k_tail) || !aligned16(v_tail) || !aligned16(o) ||
-        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-        return fail(STAR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-    return STAR_OK;
 }
 
 // One partition on the MFMA kernel (E4M3 codes when k_scale is set): its key splits, then
@@ -200,45 +103,6 @@ star_status_t query_mfma(const void* q, int32_t rows, const void* k_ctx, const v
     return ok();
 }
 
-// Chunk plan of the decode kernel and its workspace carve-up.
-struct DecodeLaunch {
-    star::DecodeChunkPlan plan;
-    float *a, *m, *l;
-    unsigned* tickets;
-};
-
-// Workspace layout: the chunk partials, then hkv 32-bit counters.  With `tickets` given, the
-// counters live there instead and the workspace holds the partials only.
-star_status_t plan_decode(const int64_t* shard_bounds, int32_t n_shards, int64_t tail_len, int64_t tail_cap,
-                          int32_t hq, int32_t hkv, int32_t d, void* workspace, size_t workspace_bytes,
-                          DecodeLaunch* dl, unsigned* tickets = nullptr) {
-    star::DecodeChunkPlan& plan = dl->plan;
-    plan = {};
-    plan.n_shards = n_shards;
-    plan.chunk = star::decode_chunk_len(shard_bounds, n_shards, hkv);
-    int64_t nc = 0;
-    for (int r = 0; r < n_shards; ++r) {
-        plan.shard_lo[r] = shard_bounds[r];
-        plan.chunk_prefix[r] = (int32_t)nc;
-        nc += (shard_bounds[r + 1] - shard_bounds[r] + plan.chunk - 1) / plan.chunk;
-    }
-    plan.shard_lo[n_shards] = shard_bounds[n_shards];
-    plan.chunk_prefix[n_shards] = (int32_t)nc;
-    nc += (tail_len + 1 + plan.chunk - 1) / plan.chunk;
-    plan.chunk_prefix[n_shards + 1] = (int32_t)nc;
-    plan.n_chunks = (int32_t)nc;
-    const int64_t n_max = star::decode_max_chunks(tail_cap, n_shards, hkv);
-    if (nc > n_max) return fail(STAR_ERR_HIP, "decode chunk plan exceeds its bound");
-    const size_t part_bytes = partials_bytes(n_max, hq, d);
-    const size_t need = part_bytes + (tickets ? 0 : round_up((size_t)hkv * 4));
-    if (!workspace || workspace_bytes < need || !aligned16(workspace))
-        return fail(STAR_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    partials_ptrs(workspace, n_max, hq, d, &dl->a, &dl->m, &dl->l);
-    dl->tickets = tickets ? tickets : reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + part_bytes);
-    return STAR_OK;
-}
-
 // ---- Scratch of star_decode_step_noalloc, for callers that cannot allocate.
 // A file-scope device array: every GPU the library runs on holds its own copy, at its own
 // address, until the process ends.  Its first kNoAllocTicketBytes hold the per-kv-head
@@ -273,17 +137,6 @@ star_status_t noalloc_scratch(void** out) {
     return STAR_OK;
 }
 
-star_status_t check_kv_fp8(const void* x, int64_t tokens, int32_t hkv, int32_t d, star_dtype_t dt) {
-    if (!x) return fail(STAR_ERR_INVALID_ARG, "x must be non-null");
-    if (tokens < 0) return fail(STAR_ERR_INVALID_ARG, "tokens (%lld) must be >= 0", (long long)tokens);
-    if (hkv < 1 || hkv > 65535) return fail(STAR_ERR_INVALID_ARG, "hkv (%d) must be in [1, 65535]", hkv);
-    if (dt != STAR_F32 && dt != STAR_BF16) return fail(STAR_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
-    if (d < 8 || d > 256 || d % 8)
-        return fail(STAR_ERR_UNSUPPORTED, "head dim %d not supported (need d %% 8 == 0 and 8 <= d <= 256)", d);
-    if (!aligned16(x)) return fail(STAR_ERR_INVALID_ARG, "x must be 16-byte aligned");
-    return STAR_OK;
-}
-
 }  // namespace
 
 extern "C" {
@@ -299,7 +152,7 @@ const char* star_status_str(star_status_t status) {
     return "STAR_ERR_UNKNOWN";
 }
 
-const char* star_last_error(void) { return g_last_error.c_str(); }
+const char* star_last_error(void) { return star::host::last_error(); }
 
 const char* star_version(void) { return "0.1.0"; }
 
