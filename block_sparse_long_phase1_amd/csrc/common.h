@@ -57,13 +57,38 @@ __device__ __forceinline__ float half_pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Value of lane (l ^ 1), (l ^ 2), mirrored inside each half row (l ^ 7 within 8 lanes) and
+// mirrored inside each row (l ^ 15 within 16 lanes): DPP moves, no LDS round trip.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xb1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4e;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Max / sum over all 64 lanes, the same bits in every lane: a butterfly inside each 16-lane
+// row by DPP, then lanes l, l^16, l^32, l^48 through the permlane swaps.  Each step pairs a
+// lane with one whose partial covers a disjoint set of lanes; the operations are commutative,
+// so both lanes of a pair form the same value.
 __device__ __forceinline__ float wave_max(float x) {
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    return x;
+    x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return half_pair_max(x);
 }
 __device__ __forceinline__ float wave_sum(float x) {
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppRowHalfMirror>(x);
+    x += dpp_f32<kDppRowMirror>(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    return half_pair_sum(x);
 }
 
 // Select bytes of the pair (hi:lo) -- v_perm_b32.

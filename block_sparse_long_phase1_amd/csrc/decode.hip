@@ -14,7 +14,8 @@
 // and the workgroup that owns it appends k_new / v_new to the query host's
 // cache (no one reads that slot from memory in the same launch).
 //
-// Each wave walks 32-key tiles of its chunk.  Both products run on
+// Each wave walks 32-key tiles of its chunk, bf16 tiles with non-temporal loads (the stream
+// is read once per step and gains nothing from the last-level cache).  Both products run on
 // v_mfma_f32_16x16x32_bf16 with the G <= 16 q heads as the 16-wide column
 // block: S^T = K Q^T takes K straight from 16-byte global loads, and
 // O^T += V^T P^T takes V^T from a wave-private LDS copy of the V tile (stored
@@ -86,6 +87,16 @@ struct TileE4m3 {
     u32x2 k[NK];
     u32x4 v[NV];
 };
+
+// A load of the bf16 K/V stream, marked non-temporal.  Every cached byte is read once per
+// step, so caching it in the last-level cache only costs bandwidth: measured on 8b_1m, the
+// same kernel streams 7.1 TB/s with these loads against 6.0 TB/s with ordinary ones.  The
+// E4M3 stream keeps ordinary loads: its K operand loads take 32 bytes of a 128-byte row
+// each, four loads per row, and marked non-temporal they ran 12% slower.
+template <typename V>
+__device__ __forceinline__ V stream_load(const V* p) {
+    return __builtin_nontemporal_load(p);
+}
 
 // Four keys of one head-dim column from a row-major LDS tile (see the kernel comment).
 __device__ __forceinline__ u32x2v lds_read_tr(const uint16_t* p) {
@@ -224,7 +235,7 @@ decode_kernel(const DecodeArgs p) {
             key = key < hi ? key : hi - 1;
             const uint16_t* src = key == new_key ? knew : kb + key * kD;
 #pragma unroll
-            for (int dd = 0; dd < kDD; ++dd) b.k[kb2 * kDD + dd] = *reinterpret_cast<const u32x4*>(src + dd * 32 + grp * 8);
+            for (int dd = 0; dd < kDD; ++dd) b.k[kb2 * kDD + dd] = stream_load(reinterpret_cast<const u32x4*>(src + dd * 32 + grp * 8));
         }
 #pragma unroll
         for (int i = 0; i < kVPieces; ++i) {
@@ -232,7 +243,7 @@ decode_kernel(const DecodeArgs p) {
             int64_t vkey = k0 + cc / kRowChunks;
             vkey = vkey < hi ? vkey : hi - 1;
             const uint16_t* vsrc = vkey == new_key ? vnew : vb + vkey * kD;
-            b.v[i] = *reinterpret_cast<const u32x4*>(vsrc + (cc % kRowChunks) * 8);
+            b.v[i] = stream_load(reinterpret_cast<const u32x4*>(vsrc + (cc % kRowChunks) * 8));
         }
         }
     };
