@@ -73,7 +73,10 @@ int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv)
     for (int r = 0; r < n_shards; ++r) {
         const int64_t len = shard_bounds[r + 1] - shard_bounds[r];
         if (len <= 0) continue;
-        int64_t cr = budget * len / (L > 0 ? L : 1);
+        // the shard's share of the budget, rounded to nearest (rounding down could halve the
+        // chunks of many equal shards: 16 shards of 1.94 chunks each would get 1 apiece)
+        const int64_t Ld = L > 0 ? L : 1;
+        int64_t cr = (2 * budget * len + Ld) / (2 * Ld);
         if (cr < 1) cr = 1;
         const int64_t need = (len + cr - 1) / cr;
         if (need > ch) ch = need;
@@ -82,8 +85,8 @@ int64_t decode_chunk_len(const int64_t* shard_bounds, int n_shards, int32_t hkv)
 }
 
 int64_t decode_max_chunks(int64_t tail_cap, int n_shards, int32_t hkv) {
-    // The plan above gives each shard at most budget*len/L chunks (at least 1), hence at
-    // most budget + n_shards context chunks, and the query host at most ceil(tail_cap / 128).
+    // The plan above gives each shard at most budget*len/L + 1/2 chunks (at least 1), hence
+    // at most budget + n_shards context chunks, and the query host at most ceil(tail_cap / 128).
     int64_t budget = 272 / hkv - 1;
     if (budget < n_shards) budget = n_shards;
     return budget + n_shards + (tail_cap + kDecodeChunkQuantum - 1) / kDecodeChunkQuantum;
