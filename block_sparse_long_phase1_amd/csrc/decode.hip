@@ -14,8 +14,8 @@
 // and the workgroup that owns it appends k_new / v_new to the query host's
 // cache (no one reads that slot from memory in the same launch).
 //
-// Each wave walks 32-key tiles of its chunk, bf16 tiles with non-temporal loads (the stream
-// is read once per step and gains nothing from the last-level cache).  Both products run on
+// Each wave walks 32-key tiles of its chunk with non-temporal loads (the stream is read once
+// per step and gains nothing from the last-level cache).  Both products run on
 // v_mfma_f32_16x16x32_bf16 with the G <= 16 q heads as the 16-wide column
 // block: S^T = K Q^T takes K straight from 16-byte global loads, and
 // O^T += V^T P^T takes V^T from a wave-private LDS copy of the V tile (stored
@@ -84,15 +84,15 @@ struct TileBf16 {
 };
 template <int NK, int NV>
 struct TileE4m3 {
-    u32x2 k[NK];
+    u32x4 k[NK];
     u32x4 v[NV];
 };
 
-// A load of the bf16 K/V stream, marked non-temporal.  Every cached byte is read once per
-// step, so caching it in the last-level cache only costs bandwidth: measured on 8b_1m, the
-// same kernel streams 7.1 TB/s with these loads against 6.0 TB/s with ordinary ones.  The
-// E4M3 stream keeps ordinary loads: its K operand loads take 32 bytes of a 128-byte row
-// each, four loads per row, and marked non-temporal they ran 12% slower.
+// A load of the K/V stream, marked non-temporal.  Every cached byte is read once per step, so
+// caching it in the last-level cache only costs bandwidth: measured on 8b_1m, the bf16 stream
+// runs at 7.1 TB/s with these loads against 6.0 TB/s with ordinary ones, and the E4M3 stream
+// at 6.9 against 5.8 TB/s.  All of them are 16-byte loads; with 8-byte E4M3 K loads the
+// non-temporal form was 12% slower instead.
 template <typename V>
 __device__ __forceinline__ V stream_load(const V* p) {
     return __builtin_nontemporal_load(p);
@@ -175,16 +175,6 @@ decode_kernel(const DecodeArgs p) {
     const uint8_t* kb8 = KV8 ? p.k8 + (int64_t)g * p.L * kD : nullptr;
     const uint8_t* vb8 = KV8 ? p.v8 + (int64_t)g * p.L * kD : nullptr;
 
-    // ---- Q^T as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (grp, col)
-    //      holds q head g*G + col (zero past G), head-dim 32*dd + 8*grp .. +7.
-    bf16x8 qb[kDD];
-#pragma unroll
-    for (int dd = 0; dd < kDD; ++dd) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (col < G) w = *reinterpret_cast<const u32x4*>(p.q_new + (int64_t)(g * G + col) * kD + dd * 32 + grp * 8);
-        qb[dd] = __builtin_bit_cast(bf16x8, w);
-    }
-
     // O^T accumulators: head-dim block db of 16 rows; lane (grp, col) holds rows 16db + 4grp + r.
     f32x4 acc[kDB];
 #pragma unroll
@@ -200,14 +190,29 @@ decode_kernel(const DecodeArgs p) {
     auto run_tiles = [&](auto f8_tag) {
     constexpr bool F8 = decltype(f8_tag)::value;
     constexpr int kV8Pieces = kT * kD / 16 / 64;   // 16-byte E4M3 V pieces per lane per tile
+    // ---- Q^T as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (grp, col)
+    //      holds q head g*G + col (zero past G) and, for head-dim block dd, the eight head-dim
+    //      entries that its K operand holds.  The contraction order over the head dim is free
+    //      as long as K and Q agree.  bf16 chunks take block dd, slot 8grp + i as head-dim
+    //      32dd + 8grp + i.  E4M3 chunks take it as 64(dd/2) + 16grp + 8(dd%2) + i, so that one
+    //      16-byte load of codes per lane covers the blocks 2j and 2j + 1.
+    bf16x8 qb[kDD];
+#pragma unroll
+    for (int dd = 0; dd < kDD; ++dd) {
+        const int off = F8 ? 64 * (dd / 2) + 16 * grp + 8 * (dd % 2) : 32 * dd + 8 * grp;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (col < G) w = *reinterpret_cast<const u32x4*>(p.q_new + (int64_t)(g * G + col) * kD + off);
+        qb[dd] = __builtin_bit_cast(bf16x8, w);
+    }
     // score scale (log2 units), with the K scale of an E4M3 chunk folded in
     const float sl2 = F8 ? p.sl2 * p.k_scale[g] : p.sl2;
-    // K operands (16-key block kb, head-dim block dd: key k0 + 16kb + col, head-dim 32dd + 8grp)
-    // and V row-major pieces for LDS, for the tile that starts at key k0.  Keys past the chunk
-    // are clamped to its last key.  E4M3 chunks load half the bytes and widen them to bf16
-    // when they are used; a wave keeps two of their tiles in flight (kDepth), so that it
-    // has as many bytes outstanding as with one bf16 tile.
-    using Tile = typename std::conditional<F8, TileE4m3<2 * kDD, kV8Pieces>, TileBf16<2 * kDD, kVPieces>>::type;
+    // K operands (16-key block kb, head-dim block dd: key k0 + 16kb + col, the head-dim order
+    // above) and V row-major pieces for LDS, for the tile that starts at key k0.  Keys past the
+    // chunk are clamped to its last key.  E4M3 chunks load half the bytes (one 16-byte load per
+    // lane for two head-dim blocks) and widen them to bf16 when they are used; a wave keeps two
+    // of their tiles in flight (kDepth), so that it has as many bytes outstanding as with one
+    // bf16 tile.
+    using Tile = typename std::conditional<F8, TileE4m3<kDD, kV8Pieces>, TileBf16<2 * kDD, kVPieces>>::type;
     constexpr int kDepth = F8 ? 2 : 1;
     Tile buf[kDepth];
     auto load_tile = [&](Tile& b, int64_t k0) {
@@ -218,15 +223,15 @@ decode_kernel(const DecodeArgs p) {
                 key = key < hi ? key : hi - 1;
                 const uint8_t* src = kb8 + key * kD;
 #pragma unroll
-                for (int dd = 0; dd < kDD; ++dd)
-                    b.k[kb2 * kDD + dd] = *reinterpret_cast<const u32x2*>(src + dd * 32 + grp * 8);
+                for (int j = 0; j < kDD / 2; ++j)
+                    b.k[kb2 * (kDD / 2) + j] = stream_load(reinterpret_cast<const u32x4*>(src + 64 * j + 16 * grp));
             }
 #pragma unroll
             for (int i = 0; i < kV8Pieces; ++i) {
                 const int cc = lane + 64 * i;
                 int64_t vkey = k0 + cc / (kD / 16);
                 vkey = vkey < hi ? vkey : hi - 1;
-                b.v[i] = *reinterpret_cast<const u32x4*>(vb8 + vkey * kD + (cc % (kD / 16)) * 16);
+                b.v[i] = stream_load(reinterpret_cast<const u32x4*>(vb8 + vkey * kD + (cc % (kD / 16)) * 16));
             }
         } else {
 #pragma unroll
@@ -261,7 +266,8 @@ decode_kernel(const DecodeArgs p) {
             for (int dd = 0; dd < kDD; ++dd) {
                 u32x4 kop;
                 if constexpr (F8)
-                    kop = e4m3x8_to_bf16x8(b.k[kb2 * kDD + dd][0], b.k[kb2 * kDD + dd][1]);
+                    kop = e4m3x8_to_bf16x8(b.k[kb2 * (kDD / 2) + dd / 2][2 * (dd % 2)],
+                                           b.k[kb2 * (kDD / 2) + dd / 2][2 * (dd % 2) + 1]);
                 else
                     kop = b.k[kb2 * kDD + dd];
                 s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop), qb[dd], s[kb2], 0, 0, 0);
