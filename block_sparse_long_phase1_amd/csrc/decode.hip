@@ -416,19 +416,22 @@ decode_kernel(const DecodeArgs p) {
     if (ticket_sh != (unsigned)(pl.n_chunks - 1)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale cached partials below
     const int nc = pl.n_chunks;
-    // One wave per q head.  The chunks are taken in batches of 64 / (D/64), and every load of
-    // a batch is issued at once (one memory round trip): lane i loads the statistics (m, l) of
-    // chunk c0 + i, and every lane loads its D/64 head-dim columns of every chunk of the
-    // batch.  The wave then forms the batch max and weights and folds the weighted columns,
-    // rescaling what earlier batches left when the max grows.
-    constexpr int kCols = D / 64;
-    constexpr int kBatch = 64 / kCols;   // 64 registers of columns per lane
+    // One wave per q head.  The chunks are taken in batches of 64, and every load of a batch is
+    // issued at once (one memory round trip): lane i loads the statistics (m, l) of chunk
+    // c0 + i, and the column loads are 16 bytes wide, so that one load instruction covers
+    // kRows = 256 / D chunk rows (D/4 lanes per row) and a batch needs 64 / kRows of them, within
+    // the per-wave limit on loads in flight.  The wave then forms the batch max and weights and
+    // folds the weighted columns, rescaling what earlier batches left when the max grows; the
+    // kRows lane groups each sum every kRows-th chunk and are added at the end.
+    constexpr int kLanesPerRow = D / 4;
+    constexpr int kRows = 64 / kLanesPerRow;
+    constexpr int kBatch = 64;
+    constexpr int kLoads = kBatch / kRows;
+    const int sub = lane / kLanesPerRow, c4 = lane % kLanesPerRow;
     for (int q = wave; q < G; q += kWaves) {
         const int h = g * G + q;
         float M = -INFINITY, W = 0.f;
-        float o[kCols];
-#pragma unroll
-        for (int e = 0; e < kCols; ++e) o[e] = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
         for (int c0 = 0; c0 < nc; c0 += kBatch) {
             const int nb = nc - c0 < kBatch ? nc - c0 : kBatch;
             float m = -INFINITY, l = 0.f;
@@ -437,43 +440,46 @@ decode_kernel(const DecodeArgs p) {
                 m = p.pm[row];
                 l = p.pl[row];
             }
-            // chunk rows are hq * D floats apart: one uniform row pointer walks them, every
-            // load uses the same per-lane offset
-            float a[kBatch][kCols];
-            const float* rowp = p.pa + ((int64_t)c0 * p.hq + h) * kD;
-            const int64_t row_step = (int64_t)p.hq * kD;
+            // chunk rows are hq * D floats apart; load jb takes row c0 + kRows*jb + sub
+            f32x4 a[kLoads];
+            const float* rowp = p.pa + ((int64_t)(c0 + sub) * p.hq + h) * kD + 4 * c4;
+            const int64_t row_step = (int64_t)kRows * p.hq * kD;
 #pragma unroll
-            for (int jb = 0; jb < kBatch; ++jb) {
-#pragma unroll
-                for (int e = 0; e < kCols; ++e) a[jb][e] = 0.f;
-                if (jb < nb) {
-#pragma unroll
-                    for (int e = 0; e < kCols; ++e) a[jb][e] = rowp[lane * kCols + e];
-                }
+            for (int jb = 0; jb < kLoads; ++jb) {
+                a[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (kRows * jb + sub < nb) a[jb] = *reinterpret_cast<const f32x4*>(rowp);
                 rowp += row_step;
             }
             const float nM = fmaxf(M, wave_max(m));
             const float so = M == -INFINITY ? 0.f : __expf(M - nM);
-            const float w = m == -INFINITY ? 0.f : l * __expf(m - nM);
+            const float w = m == -INFINITY ? 0.f : l * __expf(m - nM);   // zero past nb
             W = W * so + wave_sum(w);
+            o *= so;
 #pragma unroll
-            for (int e = 0; e < kCols; ++e) o[e] *= so;
+            for (int jb = 0; jb < kLoads; ++jb) {
+                if (kRows * jb < nb) {
+                    // the weight of chunk c0 + kRows*jb + sub
+                    float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kRows * jb));
 #pragma unroll
-            for (int jb = 0; jb < kBatch; ++jb) {
-                if (jb < nb) {
-                    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), jb));
-#pragma unroll
-                    for (int e = 0; e < kCols; ++e) o[e] = fmaf(wj, a[jb][e], o[e]);
+                    for (int r = 1; r < kRows; ++r) {
+                        const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kRows * jb + r));
+                        wj = sub == r ? wr : wj;
+                    }
+                    o += wj * a[jb];
                 }
             }
             M = nM;
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = kRows == 2 ? half_pair_sum(o[e]) : quad_sum(o[e]);
         const bool empty = M == -INFINITY || !(W > 0.f);
         const float inv = empty ? 0.f : 1.0f / W;
-        if constexpr (kCols == 2)
-            *reinterpret_cast<uint32_t*>(p.o + (int64_t)h * kD + lane * 2) = pack_bf16x2(o[0] * inv, o[1] * inv);
-        else
-            p.o[(int64_t)h * kD + lane] = to_bf16(o[0] * inv);
+        if (sub == 0) {
+            u32x2 ow;
+            ow[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+            ow[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+            *reinterpret_cast<u32x2*>(p.o + (int64_t)h * kD + 4 * c4) = ow;
+        }
         if (lane == 0 && p.lse) p.lse[h] = empty ? -INFINITY : M + __logf(W);
     }
     // ready for the next call on this stream
