@@ -13,6 +13,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libstarattn.so")
+# Profiling build: the same library with decode.hip compiled with STAR_DECODE_TIMELINE
+# (per-workgroup timestamps of each decode launch; read by decode_timeline.py).
+TIMELINE_LIB_PATH = os.path.join(PKG, "libstarattn_timeline.so")
+TIMELINE_SOURCE = "decode.hip"
 ARCH = os.environ.get("STAR_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU ops stay disabled: the kernels' fp32 math is written as scalar code.  Host
@@ -34,15 +38,29 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def _link(hipcc: str, objs: list[str], out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % res.stderr)
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source to an object under _build/ and link libstarattn.so. Always rebuilds."""
+    """Compile every source to an object under _build/ and link libstarattn.so, and the
+    profiling library libstarattn_timeline.so.  Always rebuilds."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
+    timeline_src = os.path.join(CSRC, TIMELINE_SOURCE)
+    units = [(src, os.path.basename(src) + ".o", []) for src in srcs]
+    units.append((timeline_src, TIMELINE_SOURCE + ".timeline.o", ["-DSTAR_DECODE_TIMELINE"]))
 
-    def compile_one(src: str) -> str:
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, "-x", "hip", "-c", src, "-o", obj] + HIPCC_FLAGS
+    def compile_one(unit) -> str:
+        src, name, extra = unit
+        obj = os.path.join(BUILD_DIR, name)
+        cmd = [hipcc, "-x", "hip", "-c", src, "-o", obj] + HIPCC_FLAGS + extra
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("hipcc failed for %s:\n%s" % (src, res.stderr))
@@ -50,15 +68,12 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             print(" ".join(cmd))
         return obj
 
-    jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    jobs = jobs or min(len(units), max(1, min(16, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(compile_one, srcs))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("link failed:\n%s" % res.stderr)
-    os.replace(tmp, LIB_PATH)
+        objs = list(ex.map(compile_one, units))
+    _link(hipcc, objs[:len(srcs)], LIB_PATH)
+    _link(hipcc, [o for o, (src, _, _) in zip(objs[:len(srcs)], units) if src != timeline_src] + [objs[-1]],
+          TIMELINE_LIB_PATH)
     return LIB_PATH
 
 

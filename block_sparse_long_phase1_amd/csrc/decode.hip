@@ -118,9 +118,28 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 }  // namespace
 
+#ifdef STAR_DECODE_TIMELINE
+// Profiling build only (libstarattn_timeline.so): per-workgroup timestamps of the constant
+// 100 MHz clock at fixed points of a launch, read back by star_decode_timeline_read.  Slots:
+// 0 start, 1 stream done (waves combined), 2 partial stores complete, 3 ticket drawn,
+// 4 merger past its acquire, 5 merge done; 6 holds the ticket.
+constexpr int kTimelineGroups = 4096;
+__device__ unsigned long long g_decode_timeline[kTimelineGroups][8];
+#define STAR_TIMELINE(slot, value)                                                          \
+    do {                                                                                    \
+        if (threadIdx.x == 0 && blockIdx.x < kTimelineGroups)                               \
+            g_decode_timeline[blockIdx.x][slot] = (value);                                  \
+    } while (0)
+#else
+#define STAR_TIMELINE(slot, value) \
+    do {                           \
+    } while (0)
+#endif
+
 template <int G, int D, bool KV8>
 __global__ void __launch_bounds__(kThreads, 3)
 decode_kernel(const DecodeArgs p) {
+    STAR_TIMELINE(0, __builtin_amdgcn_s_memrealtime());
     constexpr int kD = D;                 // head dim, 64 or 128
     constexpr int kVPitch = D + 16;       // bf16 per V row in LDS: 4 consecutive rows hit disjoint banks
     constexpr int kDD = D / 32;           // 32-wide head-dim blocks of the S^T products
@@ -381,6 +400,7 @@ decode_kernel(const DecodeArgs p) {
             for (int r = 0; r < 4; ++r) wo[wave][col][db * 16 + 4 * grp + r] = acc[db][r];
     }
     __syncthreads();
+    STAR_TIMELINE(1, __builtin_amdgcn_s_memrealtime());
     const float vsc = (KV8 && f8) ? p.v_scale[g] : 1.0f;   // V scale of an E4M3 chunk
     for (int idx = tid; idx < G * kD; idx += kThreads) {
         const int q = idx / kD, d = idx % kD;
@@ -411,10 +431,14 @@ decode_kernel(const DecodeArgs p) {
     // write-back of this XCD's whole L2 per workgroup, which costs more than the merge.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    STAR_TIMELINE(2, __builtin_amdgcn_s_memrealtime());
     if (tid == 0) ticket_sh = __hip_atomic_fetch_add(&p.tickets[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
+    STAR_TIMELINE(3, __builtin_amdgcn_s_memrealtime());
+    STAR_TIMELINE(6, ticket_sh);
     if (ticket_sh != (unsigned)(pl.n_chunks - 1)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale cached partials below
+    STAR_TIMELINE(4, __builtin_amdgcn_s_memrealtime());
     const int nc = pl.n_chunks;
     // One wave per q head.  The chunks are taken in batches of 64, and every load of a batch is
     // issued at once (one memory round trip): lane i loads the statistics (m, l) of chunk
@@ -482,6 +506,10 @@ decode_kernel(const DecodeArgs p) {
         }
         if (lane == 0 && p.lse) p.lse[h] = empty ? -INFINITY : M + __logf(W);
     }
+#ifdef STAR_DECODE_TIMELINE
+    __syncthreads();
+    STAR_TIMELINE(5, __builtin_amdgcn_s_memrealtime());
+#endif
     // ready for the next call on this stream
     if (tid == 0) __hip_atomic_store(&p.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -537,3 +565,18 @@ hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, cons
 }
 
 }  // namespace star
+
+#ifdef STAR_DECODE_TIMELINE
+// Profiling build only: copy the timestamps of the last decode launch to host (at most
+// 4096 workgroups x 8 slots of 8 bytes), or clear them (host == NULL).  Synchronous.
+extern "C" STAR_API int star_decode_timeline_read(void* host, size_t bytes) {
+    if (bytes > sizeof(star::g_decode_timeline)) return (int)hipErrorInvalidValue;
+    if (!host) {
+        static unsigned long long zeros[star::kTimelineGroups][8];
+        return (int)hipMemcpyToSymbol(HIP_SYMBOL(star::g_decode_timeline), zeros, sizeof(zeros), 0,
+                                      hipMemcpyHostToDevice);
+    }
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(star::g_decode_timeline), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
+

@@ -1,0 +1,150 @@
+"""Where the time of one decode launch goes, from the profiling build of the library.
+
+    python -m block_sparse_long_phase1_amd.decode_timeline [--config 8b_32k,8b_128k_needle] [--reps 4]
+
+libstarattn_timeline.so (built next to libstarattn.so) is the same library with the decode
+kernel recording, per workgroup, the constant 100 MHz clock at fixed points: start, stream done
+(waves combined into the chunk partial), partial stores complete, ticket drawn, and for the
+workgroup that merges a kv head: past its acquire fence and merge done.  This tool runs decode
+step 0 of each workload on seeded synthetic inputs of its shapes (as bench.py does), warm (the
+same step just ran) and cold (1 GiB overwritten and read back first), and prints one JSON line
+per launch and a table of medians.  Times are microseconds from the first workgroup's start.
+The in-kernel merge exists for hq/hkv <= 4; other shapes report the stream part only.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+
+import numpy as np
+
+from . import build as _build
+
+SLOTS = 8
+GROUPS = 4096
+
+
+def _load():
+    import block_sparse_long_phase1_amd as sa
+    path = _build.TIMELINE_LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError("%s not found; build it with `python -m block_sparse_long_phase1_amd.build`" % path)
+    lib = sa.load_library(path)
+    lib.star_decode_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.star_decode_timeline_read.restype = ctypes.c_int
+    sa._lib = lib   # every binding now calls the profiling build
+    return sa, lib
+
+
+def _summary(ts: np.ndarray, grid: int) -> dict:
+    t = ts[:grid].astype(np.float64)
+    t0 = t[:, 0].min()
+    us = lambda col: (t[:, col] - t0) / 100.0
+    start, stream_end = us(0), us(1)
+    stream = stream_end - start
+    r = {"workgroups": grid, "start_spread": float(start.max()),
+         "stream_median": float(np.median(stream)), "stream_max": float(stream.max()),
+         "stream_end": float(stream_end.max())}
+    if (t[:, 2] > 0).all():
+        stored, ticket = us(2), us(3)
+        r.update({"store_wait_median": float(np.median(stored - stream_end)),
+                  "store_wait_max": float((stored - stream_end).max()),
+                  "ticket_median": float(np.median(ticket - stored)), "last_ticket": float(ticket.max())})
+        merger = t[:, 5] > 0
+        if merger.any():
+            r.update({"mergers": int(merger.sum()),
+                      "merge_acquire": float(np.max(us(4)[merger] - ticket[merger])),
+                      "merge": float(np.max(us(5)[merger] - ticket[merger])),
+                      "end": float(us(5)[merger].max())})
+    return r
+
+
+def run(configs: list[str], reps: int) -> list[dict]:
+    import torch
+    sa, lib = _load()
+    from .configs import CONFIGS
+    from . import inputs as sin
+
+    dev = "cuda:0"
+    buf = np.zeros((GROUPS, SLOTS), dtype=np.uint64)
+    out = []
+    for name in configs:
+        cfg = CONFIGS[name]
+        k = sin.randn(cfg, "k_ctx", (cfg.hkv, cfg.L, cfg.d), dev)
+        v = sin.randn(cfg, "v_ctx", (cfg.hkv, cfg.L, cfg.d), dev)
+        p2 = sin.phase2_inputs(cfg, dev)
+        bounds = cfg.bounds()
+        kt = torch.zeros((cfg.hkv, cfg.tail_cap, cfg.d), dtype=k.dtype, device=dev)
+        vt = torch.zeros_like(kt)
+        kt[:, :cfg.lq] = p2["k_qry"]
+        vt[:, :cfg.lq] = p2["v_qry"]
+        ws = sa.decode_workspace(cfg.L, cfg.tail_cap, len(bounds) - 1, cfg.hq, cfg.hkv, cfg.d, dev)
+        o = torch.empty((cfg.hq, cfg.d), dtype=k.dtype, device=dev)
+        lse = torch.empty((cfg.hq,), dtype=torch.float32, device=dev)
+        st = torch.cuda.current_stream()
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+
+        def step():
+            sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds, kt, vt, cfg.lq,
+                                o=o, lse=lse, workspace=ws, stream=st)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        for rep in range(reps):
+            for mode in ("warm", "cold"):
+                if mode == "cold":
+                    flush.fill_(float(rep))
+                    torch.sum(flush, dim=0, out=sink)
+                else:
+                    step()
+                torch.cuda.synchronize()
+                assert lib.star_decode_timeline_read(None, 0) == 0
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                step()
+                b.record(st)
+                torch.cuda.synchronize()
+                assert lib.star_decode_timeline_read(buf.ctypes.data, buf.nbytes) == 0
+                grid = int((buf[:, 0] > 0).sum())
+                r = {"config": name, "mode": mode, "rep": rep, "event_us": a.elapsed_time(b) * 1e3}
+                r.update(_summary(buf, grid))
+                print(json.dumps({k2: (round(x, 2) if isinstance(x, float) else x) for k2, x in r.items()}),
+                      flush=True)
+                out.append(r)
+        del k, v, flush
+        torch.cuda.empty_cache()
+    return out
+
+
+def table(rows: list[dict]) -> str:
+    keys = ["event_us", "start_spread", "stream_median", "stream_max", "stream_end", "store_wait_median",
+            "ticket_median", "last_ticket", "merge_acquire", "merge", "end"]
+    lines = ["| workload | launch | " + " | ".join(keys) + " |", "|---|---|" + "---|" * len(keys)]
+    for name in dict.fromkeys(r["config"] for r in rows):
+        for mode in ("warm", "cold"):
+            sel = [r for r in rows if r["config"] == name and r["mode"] == mode]
+            cells = []
+            for k in keys:
+                vals = [r[k] for r in sel if k in r]
+                cells.append("%.2f" % statistics.median(vals) if vals else "-")
+            lines.append("| %s | %s | %s |" % (name, mode, " | ".join(cells)))
+    return "\n".join(lines)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", default="8b_32k,8b_128k_needle,8b_1m")
+    ap.add_argument("--reps", type=int, default=4)
+    args = ap.parse_args()
+    rows = run(args.config.split(","), args.reps)
+    print("medians over %d launches of each kind (us):" % args.reps)
+    print(table(rows))
+
+
+if __name__ == "__main__":
+    main()

@@ -47,6 +47,24 @@ def test_exports_nothing_else():
     assert funcs == declared_functions(), funcs
 
 
+def test_timeline_build_exports_the_same_entry_points_plus_its_reader():
+    """The profiling build (decode timestamps) is the product library plus one reader; the
+    product library does not carry the reader."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    if not os.path.exists(sa_build.TIMELINE_LIB_PATH):
+        sa_build.build()
+
+    def funcs(path):
+        out = subprocess.run([nm, "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+        return sorted(line.split()[-1] for line in out.splitlines() if line.split()[1:2] == ["T"])
+    assert funcs(sa_build.TIMELINE_LIB_PATH) == sorted(declared_functions() + ["star_decode_timeline_read"])
+    assert "star_decode_timeline_read" not in funcs(sa.LIB_PATH)
+
+
 def test_status_strings(lib):
     assert lib.star_status_str(0) == b"STAR_OK"
     assert lib.star_status_str(1) == b"STAR_ERR_INVALID_ARG"
