@@ -281,12 +281,19 @@ attn_mfma_kernel(const AttnMfmaArgs p) {
     constexpr int kF8PiecesPerTensor = kBN * D / 16;          // 16-byte pieces of codes per K or V tile
     constexpr int kF8Pieces = F8 ? 2 * kF8PiecesPerTensor / kThreads : 1;
     u32x4 f8buf[kF8Pieces];
+    // A piece's row and column follow from the thread index.  They are rebuilt at each use from
+    // an opaque copy of it, so that the compiler does not keep them live across the tile loop
+    // (at d = 128 the loop has no registers to spare: kept, they were spilled and reloaded
+    // every tile); unsigned and masked, the rebuild is a few shifts and masks.
     auto f8_piece = [&](int pc, int& row, int& col0, bool& is_v) __attribute__((always_inline)) {
-        const int pi = tid + pc * kThreads;
-        is_v = pi >= kF8PiecesPerTensor;
-        const int idx = is_v ? pi - kF8PiecesPerTensor : pi;
-        row = idx / (D / 16);
-        col0 = (idx % (D / 16)) * 16;
+        unsigned ut = threadIdx.x;
+        asm volatile("" : "+v"(ut));
+        ut &= kThreads - 1;
+        const unsigned pi = ut + pc * kThreads;
+        is_v = pi >= (unsigned)kF8PiecesPerTensor;
+        const unsigned idx = is_v ? pi - kF8PiecesPerTensor : pi;
+        row = (int)(idx / (D / 16));
+        col0 = (int)(idx % (D / 16)) * 16;
     };
     auto f8_load = [&](int key0) __attribute__((always_inline)) {
         const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kptr) + (int64_t)g * hstride;
