@@ -106,6 +106,32 @@ def test_decode_kv8(hq, hkv, L, bounds, lq, T, d):
         assert_lse(lse, rl, "kv8 decode LSE step %d" % t)
 
 
+@pytest.mark.parametrize("G,d", [(4, 128), (2, 64)])
+def test_decode_kv8_merge_over_many_chunks(G, d):
+    """The E4M3 decode step with one kv head and 159 chunks (shards of 7000, 1 and 12999
+    tokens, 128-key chunks, plus the query host's): the merging workgroup folds three batches
+    of partials, the last one ragged."""
+    hq, hkv, L, lq, T = G, 1, 20000, 5, 1
+    flush_print("decode kv8 many chunks", G, d)
+    cfg = _cfg(hq, hkv, L, L, d=d, lq=lq, T=T, S=3, seed=89)
+    _, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    k8, v8, ks, vs, (hk8, hv8, hks, hvs) = _oracle_cache(k, v)
+    bounds = [0, 7000, 7001, 20000]
+    k_tail = torch.zeros((hkv, lq + T, d), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :lq] = p2["k_qry"]
+    v_tail[:, :lq] = p2["v_qry"]
+    ws = sa.decode_workspace(L, lq + T, len(bounds) - 1, hq, hkv, d, DEV)
+    o, lse = sa.star_decode_step_kv8(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k8, v8, ks, vs, bounds,
+                                     k_tail, v_tail, lq, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = of8.phase2_decode_kv8(p2["q_dec"][0].cpu(), hk8, hv8, hks, hvs, bounds, k_tail.cpu(), v_tail.cpu(),
+                                   lq + 1)
+    assert_out(o, ro, "kv8 decode O")
+    assert_lse(lse, rl, "kv8 decode LSE")
+
+
 def test_decode_kv8_equals_bf16_decode_on_representable_values():
     """With unit scales and a context whose bf16 values are E4M3 values, the E4M3 decode step
     and the bf16 decode step compute the same numbers: their outputs are bit-identical."""

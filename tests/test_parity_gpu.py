@@ -361,6 +361,34 @@ def test_decode_empty_shard_and_first_token(d):
     assert_lse(lse, rl, "LSE")
 
 
+@pytest.mark.parametrize("G,d", [(1, 128), (4, 128), (2, 64), (4, 64)])
+def test_decode_merge_over_many_chunks(G, d):
+    """One kv head: the chunk plan gives it 271 context chunks' worth of budget, here 158 chunks
+    of 128 keys over shards of 7000, 1 and 12999 tokens, plus the query host's chunk (159 in
+    all).  The last workgroup of the head then merges three batches of chunk partials (64, 64,
+    31), the last one ragged against the 2 (d = 128) or 4 (d = 64) chunk rows each of its
+    16-byte loads covers.  Two consecutive steps, both checked against the oracle."""
+    hq, hkv, L, lq, T = G, 1, 20000, 5, 2
+    flush_print("decode many chunks", G, d)
+    cfg = _cfg(hq, hkv, L, L, L, d=d, lq=lq, T=T, S=3, seed=83)
+    q, k, v = sin.phase1_inputs(cfg, DEV)
+    p2 = sin.phase2_inputs(cfg, DEV)
+    bounds = [0, 7000, 7001, 20000]
+    k_tail = torch.zeros((hkv, lq + T, d), dtype=torch.bfloat16, device=DEV)
+    v_tail = torch.zeros_like(k_tail)
+    k_tail[:, :lq] = p2["k_qry"]
+    v_tail[:, :lq] = p2["v_qry"]
+    ws = sa.decode_workspace(L, lq + T, len(bounds) - 1, hq, hkv, d, DEV)
+    for t in range(T):
+        o, lse = sa.star_decode_step(p2["q_dec"][t], p2["k_dec"][t], p2["v_dec"][t], k, v, bounds, k_tail, v_tail,
+                                     lq + t, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rl = oracle.phase2_decode(p2["q_dec"][t].cpu(), k.cpu(), v.cpu(), bounds, k_tail.cpu(), v_tail.cpu(),
+                                      lq + t + 1)
+        assert_out(o, ro, "O step %d" % t)
+        assert_lse(lse, rl, "LSE step %d" % t)
+
+
 def test_decode_shard_split_invariance():
     """Any host split gives the same decode output (partition identity), to fp32 rounding."""
     cfg = _cfg(8, 2, 4096, 1024, 1024, lq=8, T=1, S=4, seed=31)
