@@ -34,8 +34,10 @@ def _status_name(status: int) -> str:
     return load_library().star_status_str(status).decode()
 
 
-def load_library(path: str | None = None):
-    """Load libstarattn.so (built in-tree by block_sparse_long_phase1_amd.build)."""
+def load_library(path: str | None = None, make_default: bool = False):
+    """Load libstarattn.so (built in-tree by block_sparse_long_phase1_amd.build).  With `path`,
+    load that build of the library instead (the profiling build, say); `make_default` then makes
+    every binding below call it."""
     global _lib
     with _lock:
         if _lib is not None and path is None:
@@ -87,7 +89,7 @@ def load_library(path: str | None = None):
         lib.star_phase2_query_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, vp, i64, i64, i32, i32,
                                               i32, ctypes.c_int, f32, vp, vp, vp, sz, vp]
         lib.star_phase2_query_kv8.restype = ctypes.c_int
-        if path is None:
+        if path is None or make_default:
             _lib = lib
         return lib
 

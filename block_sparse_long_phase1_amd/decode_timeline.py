@@ -32,10 +32,9 @@ def _load():
     path = _build.TIMELINE_LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError("%s not found; build it with `python -m block_sparse_long_phase1_amd.build`" % path)
-    lib = sa.load_library(path)
+    lib = sa.load_library(path, make_default=True)   # every binding now calls the profiling build
     lib.star_decode_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     lib.star_decode_timeline_read.restype = ctypes.c_int
-    sa._lib = lib   # every binding now calls the profiling build
     return sa, lib
 
 
