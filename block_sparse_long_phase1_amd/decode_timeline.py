@@ -6,10 +6,12 @@ libstarattn_timeline.so (built next to libstarattn.so) is the same library with 
 kernel recording, per workgroup, the constant 100 MHz clock at fixed points: start, stream done
 (waves combined into the chunk partial), partial stores complete, ticket drawn, and for the
 workgroup that merges a kv head: past its acquire fence and merge done.  This tool runs decode
-step 0 of each workload on seeded synthetic inputs of its shapes (as bench.py does), warm (the
-same step just ran) and cold (1 GiB overwritten and read back first), and prints one JSON line
-per launch and a table of medians.  Times are microseconds from the first workgroup's start.
-The in-kernel merge exists for hq/hkv <= 4; other shapes report the stream part only.
+step 0 of each workload on seeded synthetic inputs of its shapes (as bench.py does) in three ways:
+steady (the last of 16 launches issued back to back, as in a decode loop), warm (one launch after
+the same step ran and the GPU went idle) and cold (one launch after 1 GiB was overwritten and read
+back), and prints one JSON line per launch and a table of medians.  Times are microseconds from
+the first workgroup's start.  The in-kernel merge exists for hq/hkv <= 4; other shapes report the
+stream part only.
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ from . import build as _build
 
 SLOTS = 8
 GROUPS = 4096
+MODES = ("steady", "warm", "cold")
 
 
 def _load():
@@ -52,7 +55,9 @@ def _summary(ts: np.ndarray, grid: int) -> dict:
         r.update({"store_wait_median": float(np.median(stored - stream_end)),
                   "store_wait_max": float((stored - stream_end).max()),
                   "ticket_median": float(np.median(ticket - stored)), "last_ticket": float(ticket.max())})
-        merger = t[:, 5] > 0
+        # the workgroups that drew a kv head's last ticket in this launch (slot 6 holds every
+        # workgroup's ticket, so merge slots left by earlier launches are not mistaken for them)
+        merger = (t[:, 6] == t[:, 6].max()) & (t[:, 5] > 0)
         if merger.any():
             r.update({"mergers": int(merger.sum()),
                       "merge_acquire": float(np.max(us(4)[merger] - ticket[merger])),
@@ -95,7 +100,7 @@ def run(configs: list[str], reps: int) -> list[dict]:
             step()
         torch.cuda.synchronize()
         for rep in range(reps):
-            for mode in ("warm", "cold"):
+            for mode in MODES:
                 if mode == "cold":
                     flush.fill_(float(rep))
                     torch.sum(flush, dim=0, out=sink)
@@ -103,6 +108,9 @@ def run(configs: list[str], reps: int) -> list[dict]:
                     step()
                 torch.cuda.synchronize()
                 assert lib.star_decode_timeline_read(None, 0) == 0
+                if mode == "steady":
+                    for _ in range(15):
+                        step()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(st)
                 step()
@@ -125,8 +133,10 @@ def table(rows: list[dict]) -> str:
             "ticket_median", "last_ticket", "merge_acquire", "merge", "end"]
     lines = ["| workload | launch | " + " | ".join(keys) + " |", "|---|---|" + "---|" * len(keys)]
     for name in dict.fromkeys(r["config"] for r in rows):
-        for mode in ("warm", "cold"):
+        for mode in MODES:
             sel = [r for r in rows if r["config"] == name and r["mode"] == mode]
+            if not sel:
+                continue
             cells = []
             for k in keys:
                 vals = [r[k] for r in sel if k in r]

@@ -19,9 +19,11 @@ def test_summary_of_a_merged_launch():
     rows = [(0.0, 20.0, 21.0, 21.5), (0.5, 22.5, 23.0, 23.25), (2.0, 21.0, 21.75, 22.0)]
     for i, (s, e, st, tk) in enumerate(rows):
         t[i, 0], t[i, 1], t[i, 2], t[i, 3] = (_ticks(base + x) for x in (s, e, st, tk))
-        t[i, 6] = i
-    # the last ticket (workgroup 1) merges: past its acquire at +0.5 us, done at +2.5 us
+    # tickets: workgroup 1 drew the last one and merges (past its acquire at +0.5 us, done at
+    # +2.5 us); workgroup 2 still holds merge slots from an earlier launch, which must be ignored
+    t[0, 6], t[1, 6], t[2, 6] = 0, 2, 1
     t[1, 4], t[1, 5] = _ticks(base + 23.75), _ticks(base + 25.75)
+    t[2, 4], t[2, 5] = _ticks(base - 100.0), _ticks(base - 98.0)
     r = dt._summary(t, 3)
     assert r["workgroups"] == 3
     assert r["start_spread"] == pytest.approx(2.0)
