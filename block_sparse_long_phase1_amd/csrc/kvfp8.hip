@@ -10,8 +10,9 @@
 // is scale * decode(code).  The decode step reads the codes through the
 // hardware's exact E4M3 -> bf16 conversion (decode.hip).
 //
-// Both kernels stream one kv head per grid row (blockIdx.y) in 16-byte vectors;
-// they are HBM-bound (2 or 4 bytes read per element, 1 written by the quantiser).
+// Both kernels stream one kv head per grid row (blockIdx.y) in 16-byte vectors, several
+// per thread in flight; they are HBM-bound (2 or 4 bytes read per element, 1 written by
+// the quantiser).
 #include "common.h"
 #include "internal.h"
 
@@ -19,6 +20,7 @@ namespace star {
 
 namespace {
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;   // 16-byte loads in flight per thread and loop step
 
 // E4M3 code of an fp32 value (OCP E4M3: sign, 4 exponent bits with bias 7, 3 mantissa
 // bits, subnormals m/8 * 2^-6, S.1111.111 = NaN, largest finite 448).
@@ -39,6 +41,43 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
     return s | ((r >> 20) - (120u << 3));
 }
 
+// Scales whose reciprocal and products stay far from fp32 underflow and overflow:
+// [2^-90, 2^90] as bit patterns.  Inside, clamped_quotient() is exact wherever it decides
+// the code; outside, the quantiser divides with __fdiv_rn.
+constexpr uint32_t kFastScaleLo = 0x12800000u;
+constexpr uint32_t kFastScaleHi = 0x6c800000u;
+
+// The quotient ax / s (ax = |x|, s in the range above, r = RN(1/s)) clamped to 448, in the
+// form the hardware conversion takes.  ax * r is within two ulps of ax / s; two
+// Newton-Raphson corrections with exact remainders (fma) make it faithful and then correctly
+// rounded (Markstein's theorem: a faithful quotient plus the remainder times the correctly
+// rounded reciprocal, rounded once, is the correctly rounded quotient).  Far outside the
+// E4M3 range the corrections may lose accuracy or give NaN (an infinite x, or ax / s past
+// the fp32 range), where the code no longer depends on it: below 2^-12 every value rounds
+// to zero, and fminf maps anything at or above 448 (and NaN) to 448, the saturated code.
+// A NaN x is passed through as NaN.  The GPU tests compare the codes with the oracle's for
+// every bf16 value and for fp32 values at and around every E4M3 rounding midpoint, under
+// scales on both sides of the range above.
+__device__ __forceinline__ float clamped_quotient(uint32_t axb, float s, float r) {
+    const float ax = __uint_as_float(axb);
+    const float q0 = ax * r;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, ax), r, q0);
+    const float q2 = __builtin_fmaf(__builtin_fmaf(-q1, s, ax), r, q1);
+    return axb > 0x7f800000u ? ax : __builtin_fminf(q2, 448.0f);
+}
+
+// Four E4M3 codes (bytes in element order) of clamped quotients: the hardware conversion
+// rounds to nearest even, subnormals included, exactly as the rule above for every value
+// in [0, 448] (compared over every fp32 value there), and turns NaN into 0xFF.  The sign bits are then those of x (x / s with s > 0
+// has the sign of x, NaN included), so a NaN becomes 0x7F or 0xFF by its own sign.
+__device__ __forceinline__ uint32_t e4m3x4(const float (&q)[4], const uint32_t (&xb)[4]) {
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c, true);
+    const uint32_t sign = ((xb[0] >> 24) & 0x80u) | ((xb[1] >> 16) & 0x8000u) | ((xb[2] >> 8) & 0x800000u) |
+                          (xb[3] & 0x80000000u);
+    return ((uint32_t)c & 0x7f7f7f7fu) | sign;
+}
+
 __global__ void __launch_bounds__(kThreads) kv_bits_zero_kernel(uint32_t* bits, int n) {
     for (int i = threadIdx.x; i < n; i += kThreads) bits[i] = 0u;
 }
@@ -54,17 +93,23 @@ __global__ void __launch_bounds__(kThreads) kv_absmax_kernel(const void* x, int6
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(x) +
                                                       (size_t)g * per_head * (BF16 ? 2 : 4));
     uint32_t m = 0u;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads) {
-        const u32x4 w = src[i];
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += kUnroll * stride) {
+        u32x4 w[kUnroll];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (BF16) {
-                m = max(m, (w[j] << 16) & 0x7fffffffu);
-                m = max(m, w[j] & 0x7fff0000u);
-            } else {
-                m = max(m, w[j] & 0x7fffffffu);
+        for (int u = 0; u < kUnroll; ++u)
+            w[u] = i + u * stride < nvec ? __builtin_nontemporal_load(src + i + u * stride) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (BF16) {
+                    m = max(m, (w[u][j] << 16) & 0x7fffffffu);
+                    m = max(m, w[u][j] & 0x7fff0000u);
+                } else {
+                    m = max(m, w[u][j] & 0x7fffffffu);
+                }
             }
-        }
     }
 #pragma unroll
     for (int sh = 32; sh > 0; sh >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, sh));
@@ -87,16 +132,69 @@ __global__ void __launch_bounds__(kThreads) kv_scale_from_bits_kernel(uint32_t* 
     }
 }
 
-// 8 elements per thread step: one (bf16) or two (fp32) 16-byte loads, one 8-byte store.
+// Eight elements as fp32 bit patterns from one (bf16) or two (fp32) 16-byte vectors.
+template <bool BF16>
+__device__ __forceinline__ void widen8(const u32x4 (&w)[2], uint32_t (&xb)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (BF16) {
+            xb[2 * j] = w[0][j] << 16;
+            xb[2 * j + 1] = w[0][j] & 0xffff0000u;
+        } else {
+            xb[j] = w[0][j];
+            xb[4 + j] = w[1][j];
+        }
+    }
+}
+
+// 8 elements per thread step: one (bf16) or two (fp32) 16-byte loads, one 8-byte store;
+// kUnroll steps' loads are issued before any is used.
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) kv_quantize_kernel(const void* x, int64_t per_head, const float* scale,
                                                                uint8_t* out) {
+    constexpr int kVec = BF16 ? 1 : 2;   // 16-byte vectors per 8 elements
     const int g = blockIdx.y;
     const float s = scale[g];
     const int64_t n8 = per_head / 8;
     const char* src = static_cast<const char*>(x) + (size_t)g * per_head * (BF16 ? 2 : 4);
+    const u32x4* sv = reinterpret_cast<const u32x4*>(src);
     u32x2* dst = reinterpret_cast<u32x2*>(out + (size_t)g * per_head);
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t sbits = __float_as_uint(s);
+    if (sbits >= kFastScaleLo && sbits <= kFastScaleHi) {   // the same for the whole grid row
+        const float r = __fdiv_rn(1.0f, s);
+        for (int64_t i = i0; i < n8; i += kUnroll * stride) {
+            u32x4 w[kUnroll][2];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int h = 0; h < kVec; ++h)
+                    w[u][h] = i + u * stride < n8 ? __builtin_nontemporal_load(sv + kVec * (i + u * stride) + h)
+                                                  : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (i + u * stride >= n8) continue;
+                uint32_t xb[8];
+                widen8<BF16>(w[u], xb);
+                u32x2 o;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float q[4];
+                    uint32_t xh[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        xh[j] = xb[4 * h + j];
+                        q[j] = clamped_quotient(xh[j] & 0x7fffffffu, s, r);
+                    }
+                    o[h] = e4m3x4(q, xh);
+                }
+                __builtin_nontemporal_store(o, dst + i + u * stride);
+            }
+        }
+        return;
+    }
+    for (int64_t i = i0; i < n8; i += stride) {
         float v[8];
         if (BF16) {
             const u32x4 w = reinterpret_cast<const u32x4*>(src)[i];
@@ -124,9 +222,11 @@ __global__ void __launch_bounds__(kThreads) kv_quantize_kernel(const void* x, in
     }
 }
 
-dim3 stream_grid(int64_t vecs, int hkv) {
+// Workgroups per kv head: enough for the vectors, at most `total` over all heads (about 4
+// (abs-max) or 8 (quantiser) per CU, the best measured).
+dim3 stream_grid(int64_t vecs, int hkv, int total) {
     int64_t nb = (vecs + kThreads - 1) / kThreads;
-    const int64_t cap = (2048 + hkv - 1) / hkv;   // about 8 workgroups per CU in all
+    const int64_t cap = (total + hkv - 1) / hkv;
     if (nb > cap) nb = cap;
     if (nb < 1) nb = 1;
     return dim3((unsigned)nb, (unsigned)hkv);
@@ -140,7 +240,7 @@ hipError_t launch_kv_fp8_scales(const void* x, int64_t tokens, int hkv, int d, b
     uint32_t* bits = reinterpret_cast<uint32_t*>(scale);
     hipLaunchKernelGGL(kv_bits_zero_kernel, dim3(1), dim3(kThreads), 0, stream, bits, hkv);
     if (per_head > 0) {
-        const dim3 grid = stream_grid(per_head / (bf16 ? 8 : 4), hkv);
+        const dim3 grid = stream_grid(per_head / (bf16 ? 8 : 4), hkv, 1024);
         if (bf16)
             hipLaunchKernelGGL(kv_absmax_kernel<true>, grid, dim3(kThreads), 0, stream, x, per_head, bits);
         else
@@ -155,7 +255,7 @@ hipError_t launch_kv_quantize_fp8(const void* x, int64_t tokens, int hkv, int d,
     if (hkv < 1 || hkv > 65535 || tokens < 0 || d % 8) return hipErrorInvalidValue;
     const int64_t per_head = tokens * d;
     if (per_head == 0) return hipSuccess;
-    const dim3 grid = stream_grid(per_head / 8, hkv);
+    const dim3 grid = stream_grid(per_head / 8, hkv, 2048);
     if (bf16)
         hipLaunchKernelGGL(kv_quantize_kernel<true>, grid, dim3(kThreads), 0, stream, x, per_head, scale, out);
     else

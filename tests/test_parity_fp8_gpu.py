@@ -77,6 +77,69 @@ def test_codes_at_format_edges(dtype):
     assert bad.size == 0, [(float(x[tuple(i)]), hex(got[tuple(i)]), hex(rc[tuple(i)])) for i in bad[:8]]
 
 
+def _scales_both_sides_of_the_fast_range():
+    """Scales for the quantiser tests: max / 448 of seeded bf16 maxima, seeded fp32 scales
+    over 2^-120 .. 2^120, and fixed ones at and just past 2^-90 and 2^90 (the ends of the
+    kernel's reciprocal path; outside it divides), 1, 3, the smallest normal and subnormal
+    and the largest finite fp32."""
+    rng = np.random.default_rng(97)
+    maxima = (rng.integers(1, 0x7F80, size=96).astype(np.uint32) << 16).view(np.float32)
+    from_bf16 = (maxima / np.float32(448.0)).astype(np.float32)
+    rand = np.exp2(rng.uniform(-120, 120, size=32)).astype(np.float32)
+    lo, hi = np.float32(2.0 ** -90), np.float32(2.0 ** 90)
+    fixed = np.float32([1.0, 3.0, lo, np.nextafter(lo, np.float32(0)), hi, np.nextafter(hi, np.float32(np.inf)),
+                        2.0 ** -126, np.float32(2.0 ** -149), np.finfo(np.float32).max])
+    return np.concatenate([from_bf16, rand, fixed]).astype(np.float32)
+
+
+def test_codes_every_bf16_value_under_many_scales():
+    """Every bf16 bit pattern (finite, infinite, NaN, both signs) quantised under each scale of
+    the set above: codes bit-exact against the oracle's."""
+    sc = _scales_both_sides_of_the_fast_range()
+    flush_print("kv fp8 every bf16 value", len(sc), "scales")
+    pats = np.arange(1 << 16, dtype=np.uint16).view(np.int16).reshape(1, -1, 8)
+    x = torch.from_numpy(np.repeat(pats, len(sc), axis=0)).view(torch.bfloat16)
+    c = sa.star_kv_quantize_fp8(x.to(DEV), torch.from_numpy(sc).to(DEV))
+    torch.cuda.synchronize()
+    rc = of8.kv_quantize(x, sc)
+    got = c.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, "%d codes differ: %s" % (len(bad), [
+        (hex(int(pats.reshape(-1)[i[1] * 8 + i[2]]) & 0xFFFF), float(sc[i[0]]), hex(got[tuple(i)]), hex(rc[tuple(i)]))
+        for i in bad[:8]])
+
+
+def test_codes_fp32_around_every_midpoint_under_many_scales():
+    """fp32 values x = RN(t * scale) for every E4M3 value and every midpoint between neighbours
+    t, moved by -4 .. +4 ulps, both signs, plus zeros, infinities, NaN and values far past the
+    range, under each scale of the set above: codes bit-exact against the oracle's."""
+    sc = _scales_both_sides_of_the_fast_range()
+    flush_print("kv fp8 fp32 midpoints", len(sc), "scales")
+    mags = of8.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    t = np.concatenate([mags, (mags[:-1] + mags[1:]) / 2, [464.0, 1e3, 2.0 ** -10, 2.0 ** -11]])
+    rows = []
+    for s in sc:
+        base = (t * np.float64(s)).astype(np.float32)
+        near = (base.view(np.int32)[:, None] + np.arange(-4, 5, dtype=np.int32)[None, :]).reshape(-1)
+        v = near.view(np.float32)
+        v = v[np.isfinite(v) & (near >= 0)]
+        extra = np.float32([0.0, np.inf, np.nan, np.finfo(np.float32).max, 1e-45])
+        rows.append(np.concatenate([v, -v, extra, -extra]))
+    n = max(len(r) for r in rows)
+    n += (-n) % 8
+    x = np.zeros((len(sc), n), np.float32)
+    for g, r in enumerate(rows):
+        x[g, :len(r)] = r
+    x = x.reshape(len(sc), -1, 8)
+    c = sa.star_kv_quantize_fp8(torch.from_numpy(x).to(DEV), torch.from_numpy(sc).to(DEV))
+    torch.cuda.synchronize()
+    rc = of8.kv_quantize(x, sc)
+    got = c.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, "%d codes differ: %s" % (len(bad), [
+        (float(x[tuple(i)]), float(sc[i[0]]), hex(got[tuple(i)]), hex(rc[tuple(i)])) for i in bad[:8]])
+
+
 @pytest.mark.parametrize("hq,hkv,L,bounds,lq,T,d", [
     (8, 2, 3000, [0, 800, 1600, 3000], 40, 3, 128),         # G = 4, ragged shards
     (16, 1, 2333, [0, 700, 700, 2333], 5, 3, 64),           # d = 64, G = 16, an empty shard
