@@ -555,7 +555,8 @@ hipError_t launch_decode_bf16(const uint16_t* q_new, const uint16_t* k_new, cons
     const dim3 gd((unsigned)grid);
     // Up to four q heads per kv head, the last chunk of each kv head merges in the same launch
     // (one wave per q head).  With more, a wave would merge several q heads one after the
-    // other; merge_kernel over the same partials (one workgroup per q head) is then faster.
+    // other, which measured no faster than merge_kernel over the same partials (one
+    // workgroup per q head) in a second launch.
     a.merge_here = a.G <= kWaves;
     hipError_t e = hipErrorInvalidValue;
     if (d == 128) e = kv8 ? launch_decode_g<128, true>(a, gd, stream) : launch_decode_g<128, false>(a, gd, stream);
