@@ -1,6 +1,6 @@
 """Where the time of one decode launch goes, from the profiling build of the library.
 
-    python -m block_sparse_long_phase1_amd.decode_timeline [--config 8b_32k,8b_128k_needle] [--reps 4]
+    python -m block_sparse_long_phase1_amd.decode_timeline [--config 8b_32k,8b_128k_needle] [--reps 4] [--kv8]
 
 libstarattn_timeline.so (built next to libstarattn.so) is the same library with the decode
 kernel recording, per workgroup, the constant 100 MHz clock at fixed points: start, stream done
@@ -11,7 +11,8 @@ steady (the last of 16 launches issued back to back, as in a decode loop), warm 
 the same step ran and the GPU went idle) and cold (one launch after 1 GiB was overwritten and read
 back), and prints one JSON line per launch and a table of medians.  Times are microseconds from
 the first workgroup's start.  The in-kernel merge exists for hq/hkv <= 4; other shapes report the
-stream part only.
+stream part only.  With --kv8 the context cache is first quantised to E4M3 (per-kv-head scales)
+and the decode step over it is timed instead (workload names get a "_kv8" suffix).
 """
 from __future__ import annotations
 
@@ -66,7 +67,7 @@ def _summary(ts: np.ndarray, grid: int) -> dict:
     return r
 
 
-def run(configs: list[str], reps: int) -> list[dict]:
+def run(configs: list[str], reps: int, kv8: bool = False) -> list[dict]:
     import torch
     sa, lib = _load()
     from .configs import CONFIGS
@@ -92,9 +93,18 @@ def run(configs: list[str], reps: int) -> list[dict]:
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         sink = torch.empty((), dtype=torch.float32, device=dev)
 
-        def step():
-            sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds, kt, vt, cfg.lq,
-                                o=o, lse=lse, workspace=ws, stream=st)
+        if kv8:
+            ks, vs = sa.star_kv_fp8_scales(k), sa.star_kv_fp8_scales(v)
+            k8, v8 = sa.star_kv_quantize_fp8(k, ks), sa.star_kv_quantize_fp8(v, vs)
+
+            def step():
+                sa.star_decode_step_kv8(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k8, v8, ks, vs, bounds, kt,
+                                        vt, cfg.lq, o=o, lse=lse, workspace=ws, stream=st)
+        else:
+            def step():
+                sa.star_decode_step(p2["q_dec"][0], p2["k_dec"][0], p2["v_dec"][0], k, v, bounds, kt, vt, cfg.lq,
+                                    o=o, lse=lse, workspace=ws, stream=st)
+        label = name + ("_kv8" if kv8 else "")
 
         for _ in range(3):
             step()
@@ -118,12 +128,14 @@ def run(configs: list[str], reps: int) -> list[dict]:
                 torch.cuda.synchronize()
                 assert lib.star_decode_timeline_read(buf.ctypes.data, buf.nbytes) == 0
                 grid = int((buf[:, 0] > 0).sum())
-                r = {"config": name, "mode": mode, "rep": rep, "event_us": a.elapsed_time(b) * 1e3}
+                r = {"config": label, "mode": mode, "rep": rep, "event_us": a.elapsed_time(b) * 1e3}
                 r.update(_summary(buf, grid))
                 print(json.dumps({k2: (round(x, 2) if isinstance(x, float) else x) for k2, x in r.items()}),
                       flush=True)
                 out.append(r)
         del k, v, flush
+        if kv8:
+            del k8, v8
         torch.cuda.empty_cache()
     return out
 
@@ -149,8 +161,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", default="8b_32k,8b_128k_needle,8b_1m")
     ap.add_argument("--reps", type=int, default=4)
+    ap.add_argument("--kv8", action="store_true", help="time the decode step over an E4M3 context cache")
     args = ap.parse_args()
-    rows = run(args.config.split(","), args.reps)
+    rows = run(args.config.split(","), args.reps, args.kv8)
     print("medians over %d launches of each kind (us):" % args.reps)
     print(table(rows))
 
