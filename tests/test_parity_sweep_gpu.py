@@ -4,7 +4,8 @@ The cases are drawn once from a fixed seed (so a failure names a reproducible ca
 GQA group sizes, head dims (the MFMA path at 64 and 128, the vector path at 96), context
 lengths, block and anchor sizes (anchor from 0 to block, blocks longer than the context),
 shard splits with empty shards, numbers of cached query tokens and decode steps, and bf16 or
-E4M3 context caches.  Sizes stay small enough for the fp64 oracle to finish in seconds.
+E4M3 context caches.  Sizes stay small enough for the fp64 oracle to finish in seconds.  A
+second draw from another seed repeats the mix with contexts three to four times longer.
 """
 import random
 
@@ -29,51 +30,57 @@ def _bounds(rng, L, S):
     return [0] + cuts + [L]
 
 
-def _phase1_cases(n):
+def _phase1_cases(n, rng=_RNG, max_len=2000):
     out = []
     for _ in range(n):
-        hkv = _RNG.choice([1, 2, 4])
-        G = _RNG.choice([1, 2, 4, 8, 16])
-        d = _RNG.choice([64, 128, 128, 96])
-        L = _RNG.randint(1, 2000 if hkv * G <= 8 else 900)
-        block = _RNG.randint(1, L + 100)
-        anchor = _RNG.randint(0, block)
+        hkv = rng.choice([1, 2, 4])
+        G = rng.choice([1, 2, 4, 8, 16])
+        d = rng.choice([64, 128, 128, 96])
+        L = rng.randint(1, max_len if hkv * G <= 8 else max_len * 9 // 20)
+        block = rng.randint(1, L + 100)
+        anchor = rng.randint(0, block)
         out.append((hkv * G, hkv, L, block, anchor, d))
     return out
 
 
-def _decode_cases(n):
+def _decode_cases(n, rng=_RNG, max_len=5000):
     out = []
     for _ in range(n):
-        hkv = _RNG.choice([1, 2, 4])
-        G = _RNG.choice([1, 2, 4, 8, 16])
-        kv8 = _RNG.random() < 0.5
-        d = _RNG.choice([64, 128] if kv8 else [64, 128, 96])
-        L = _RNG.randint(1, 5000)
-        S = _RNG.randint(1, 6)
-        lq = _RNG.randint(0, 60)
-        T = _RNG.randint(1, 3)
-        out.append((hkv * G, hkv, L, _bounds(_RNG, L, S), lq, T, d, kv8))
+        hkv = rng.choice([1, 2, 4])
+        G = rng.choice([1, 2, 4, 8, 16])
+        kv8 = rng.random() < 0.5
+        d = rng.choice([64, 128] if kv8 else [64, 128, 96])
+        L = rng.randint(1, max_len)
+        S = rng.randint(1, 6)
+        lq = rng.randint(0, 60)
+        T = rng.randint(1, 3)
+        out.append((hkv * G, hkv, L, _bounds(rng, L, S), lq, T, d, kv8))
     return out
 
 
-def _query_cases(n):
+def _query_cases(n, rng=_RNG, max_len=4000):
     out = []
     for _ in range(n):
-        hkv = _RNG.choice([1, 2, 4])
-        G = _RNG.choice([1, 2, 4, 8])
-        d = _RNG.choice([64, 128])
-        L = _RNG.randint(1, 4000)
-        S = _RNG.randint(1, 5)
-        tail_len = _RNG.randint(1, 300)
-        rows = _RNG.randint(1, tail_len)
-        out.append((hkv * G, hkv, L, _bounds(_RNG, L, S), rows, tail_len, d))
+        hkv = rng.choice([1, 2, 4])
+        G = rng.choice([1, 2, 4, 8])
+        d = rng.choice([64, 128])
+        L = rng.randint(1, max_len)
+        S = rng.randint(1, 5)
+        tail_len = rng.randint(1, 300)
+        rows = rng.randint(1, tail_len)
+        out.append((hkv * G, hkv, L, _bounds(rng, L, S), rows, tail_len, d))
     return out
 
 
 PHASE1 = _phase1_cases(14)
 DECODE = _decode_cases(12)
 QUERY = _query_cases(8)
+# A second draw from a generator of its own, with contexts up to three or four times longer
+# (more tiles and key splits per case); the lists above stay as drawn.
+_RNG_MORE = random.Random(20261204)
+PHASE1 += _phase1_cases(14, _RNG_MORE, max_len=6000)
+DECODE += _decode_cases(12, _RNG_MORE, max_len=20000)
+QUERY += _query_cases(8, _RNG_MORE, max_len=12000)
 
 
 def _query_kv8_cases(n):
